@@ -1,0 +1,9 @@
+"""Seeded synthetic inputs shared by the CPU oracle and the GPU path.
+
+This package only draws numbers and lays out index arrays (context lengths,
+block tables, which token rows each write covers). It holds none of the
+method's arithmetic: no slot computation, no gather, no attention. Both the
+oracle (``oracle/``) and the HIP path consume what it returns.
+"""
+
+from .gen import CONFIGS, Workload, kv_bytes, make_custom, make_workload, poison_pool  # noqa: F401
