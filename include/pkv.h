@@ -1,0 +1,218 @@
+/*
+ * pkv.h -- paged KV cache write and paged attention for AMD MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels. Every data pointer is a DEVICE
+ * pointer owned by the caller; descriptor structs are HOST pointers read
+ * during the call. The library allocates nothing, keeps no state between
+ * calls, never synchronises and never reads device memory on the host: each
+ * entry point validates its scalar arguments, enqueues kernels on `stream`
+ * (a hipStream_t; NULL is the null stream) and returns. Buffers must stay alive
+ * until that work completes. Every entry point returns a pkv_status; on error
+ * nothing is enqueued and pkv_last_error() names the offending argument.
+ *
+ * Sources for what is computed (page titles as they appear on the pages):
+ *  [MV]  "Build a Mini vLLM: Paged KV Cache and Continuous Batching From
+ *        Scratch": section 2 "The paged KV cache" (block pool, per-sequence
+ *        block table, append_slot -> (table[pos // BLOCK], pos % BLOCK));
+ *        section 3 "PagedAttention" (gather K/V through the table in logical
+ *        order, GQA by repeating KV heads onto query heads, softmax(q.k/sqrt(hd)),
+ *        weighted sum of V); section 4 (prefill writes every token's K/V into
+ *        its slot and attends with a causal -inf mask; decode writes one token
+ *        per sequence, then attends).
+ *  [D16] "Day 16: the paged KV cache, real K/V through scattered blocks":
+ *        "What I added today" (per-layer flat pool
+ *        [num_blocks * block_size, num_kv_heads, head_dim], each token at the
+ *        flat slot its table assigns); "What I learned" items 1-3 (one table
+ *        shared by all layers; write = scatter; read = gather).
+ *  [NV]  "nano-vLLM": "How it works" (pool [blocks, 16, kv_heads, hd]; write
+ *        at table[n // 16], slot n % 16; short tables padded with the dummy
+ *        block 0; query heads grouped onto their shared K/V head; masked
+ *        attention), "Where the time went" (a real kernel reads the blocks in
+ *        place instead of gathering a copy).
+ *
+ * Layouts (all row-major, contiguous, element type `dtype`):
+ *   pool:   k_pool, v_pool  [num_blocks, block_size, num_kv_heads, head_dim]
+ *           (one pair per layer; a layered pool is passed as a per-layer
+ *           pointer). Flat slot s = block * block_size + offset addresses
+ *           row s of the [num_blocks * block_size, num_kv_heads, head_dim] view.
+ *   k, v:   [num_tokens, num_kv_heads, head_dim]
+ *   q, out: [num_seqs, num_q_heads, head_dim]            (decode)
+ *           [total_q_rows, num_q_heads, head_dim]        (prefill, packed)
+ *   block_tables: int32 [num_seqs, max_blocks_per_seq]; entries past a
+ *           sequence's last block are never read (pad them with 0).
+ *   context_lens, slot_mapping, first_pos, cu_*: int32.
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ * The context length of a sequence counts the token being decoded: write the
+ * new K/V first, then attend ([MV] section 4).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  PKV_ERR_DTYPE = 2,       /* dtype is not PKV_F32 or PKV_BF16                    */
+  PKV_ERR_SHAPE = 3,       /* sizes inconsistent or negative                      */
+  PKV_ERR_UNSUPPORTED = 4, /* valid but outside the compiled set (head_dim,
+                              group size, block size)                             */
+  PKV_ERR_WORKSPACE = 5,   /* decode workspace missing or too small              */
+  PKV_ERR_HIP = 6,         /* the HIP runtime rejected a launch                   */
+  PKV_ERR_ALIGN = 7        /* a pointer is not 16-byte aligned where required     */
+} pkv_status;
+
+typedef enum pkv_dtype { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+/* One layer's pool pair. block_size is a power of two in [1, 256];
+ * num_blocks * block_size < 2^31. */
+typedef struct pkv_pool_desc {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype; /* pkv_dtype */
+} pkv_pool_desc;
+
+/* ---------------------------------------------------------------------------
+ * pkv_slot_mapping -- flat slot of every token a write will place.
+ * [MV] section 2 (append_slot), [D16] "What I added today" (flat slot),
+ * [NV] "How it works" (table[n // 16], slot n % 16).
+ *
+ * Segment w (0 <= w < num_segments) places tokens cu_tokens[w] ..
+ * cu_tokens[w+1]-1 at consecutive logical positions first_pos[w], ... of the
+ * sequence whose table is row w of `tables` ([num_segments, max_blocks_per_seq]).
+ * Output: slot_mapping[t] = tables[w][p / block_size] * block_size
+ * + p % block_size, or -1 when p < 0, p / block_size >= max_blocks_per_seq,
+ * or the table entry is outside [0, num_blocks). Tokens past num_tokens are
+ * not written. Device pointers: tables, first_pos, cu_tokens (num_segments+1
+ * entries, non-decreasing, starting at 0), slot_mapping (num_tokens entries).
+ * One table per decode step serves every layer ([D16] "What I learned" 1-2),
+ * so a caller builds this once per step and passes it to each layer's write.
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_slot_mapping(const int32_t* tables, int32_t max_blocks_per_seq,
+                            int32_t num_segments, const int32_t* first_pos,
+                            const int32_t* cu_tokens, int32_t num_tokens,
+                            int32_t block_size, int32_t num_blocks,
+                            int32_t* slot_mapping, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * pkv_write -- scatter new K/V rows into the pool ([D16] "What I learned"
+ * item 3: write is a scatter, pool[slots] = k; [MV] section 4).
+ *
+ * For each t < num_tokens with 0 <= slot_mapping[t] < num_blocks*block_size:
+ * row slot_mapping[t] of k_pool (v_pool) receives row t of k (v), copied bit
+ * for bit. Other slots are skipped (nothing written). Slots must be distinct
+ * within a call; if not, one of the duplicates' rows lands (unspecified which).
+ * k, v, k_pool, v_pool: dtype of `pool`; any alignment of the element size
+ * (16-byte aligned rows take the vector path).
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_write(const void* k, const void* v, const int32_t* slot_mapping,
+                     int32_t num_tokens, void* k_pool, void* v_pool,
+                     const pkv_pool_desc* pool, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Paged decode attention ([MV] section 3; [NV] "How it works"), reading each
+ * sequence's blocks in place (no gathered copy).
+ *
+ * out[s][h] = sum_p softmax_p(scale * q[s][h] . K_s[p]) V_s[p][...] over
+ * positions p < context_lens[s], where K_s[p] (V_s[p]) is row
+ * block_tables[s][p / block_size] * block_size + p % block_size of k_pool
+ * (v_pool), KV head h / (num_q_heads / num_kv_heads). Accumulation is fp32;
+ * a bf16 result is rounded to nearest even.
+ *
+ * Sequences are cut into splits of `partition` tokens (a multiple of the
+ * block size; 0 picks one from the sizes, see pkv_decode_partition). Each
+ * split yields a partial (running max m in log2 units, exp-sum l, unnormalised
+ * o) in `workspace`; a second kernel merges the partials of sequences that
+ * have more than one split. Sequences with a single split are written
+ * directly. workspace (device) must hold pkv_decode_workspace_bytes(...)
+ * bytes; it may be NULL when that is 0. Its contents need no initialisation.
+ *
+ * context_lens[s] is clamped to [0, min(max_context_len,
+ * max_blocks_per_seq * block_size)]; a sequence of length 0 gets zeros.
+ * max_context_len must not exceed max_blocks_per_seq * block_size.
+ * A needed table entry outside [0, num_blocks) removes that block's tokens
+ * from the softmax (no out-of-bounds read). Slots of a block past the
+ * sequence's length may hold anything (NaN included): they are masked by
+ * selection, never multiplied in ([NV] "Correctness").
+ * q, out, k_pool, v_pool must be 16-byte aligned.
+ * Compiled set: head_dim in {16, 32, 64, 128, 256}; num_q_heads / num_kv_heads
+ * in 1..8; block_size a power of two <= 256.
+ * ------------------------------------------------------------------------- */
+int32_t pkv_decode_partition(int32_t num_seqs, int32_t max_context_len,
+                             const pkv_pool_desc* pool);
+
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t max_context_len, int32_t partition,
+                                  const pkv_pool_desc* pool);
+
+pkv_status pkv_decode(const void* q, int32_t num_seqs, int32_t num_q_heads,
+                      const void* k_pool, const void* v_pool,
+                      const pkv_pool_desc* pool, const int32_t* block_tables,
+                      int32_t max_blocks_per_seq, const int32_t* context_lens,
+                      int32_t max_context_len, float scale, int32_t partition,
+                      void* out, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* The two phases of pkv_decode, for callers that time or schedule them
+ * separately. Call both, in this order, with identical arguments. */
+pkv_status pkv_decode_partials(const void* q, int32_t num_seqs, int32_t num_q_heads,
+                               const void* k_pool, const void* v_pool,
+                               const pkv_pool_desc* pool,
+                               const int32_t* block_tables,
+                               int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t max_context_len,
+                               float scale, int32_t partition, void* out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+pkv_status pkv_decode_reduce(const void* q, int32_t num_seqs, int32_t num_q_heads,
+                             const void* k_pool, const void* v_pool,
+                             const pkv_pool_desc* pool, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t max_context_len,
+                             float scale, int32_t partition, void* out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * pkv_prefill -- causal attention of a chunk of query rows over the pool
+ * ([MV] section 4: scores + full((T,T), -inf).triu(1), softmax, weighted V).
+ *
+ * Sequence s owns packed query rows cu_q[s] .. cu_q[s+1]-1 (n_s rows). Row i
+ * sits at absolute position a = context_lens[s] - n_s + i and attends the
+ * sequence's positions 0..a through its block table (its own K/V must already
+ * be in the pool: write, then attend). Rows with a < 0 are zero.
+ * cu_q: device int32 [num_seqs+1], non-decreasing from 0, cu_q[num_seqs] ==
+ * total_q_rows; max_q_len >= every n_s. bf16 pools use bf16 matrix cores
+ * (fp32 accumulation, probabilities rounded to bf16 for the PV product);
+ * fp32 pools use fp32 vector arithmetic throughout.
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_prefill(const void* q, const int32_t* cu_q, int32_t num_seqs,
+                       int32_t num_q_heads, int32_t max_q_len, int32_t total_q_rows,
+                       const void* k_pool, const void* v_pool,
+                       const pkv_pool_desc* pool, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens,
+                       int32_t max_context_len, float scale, void* out,
+                       void* stream);
+
+/* Human-readable name of a status. Never NULL. */
+const char* pkv_status_string(pkv_status status);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* PKV_ABI_VERSION of the built library. */
+int32_t pkv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,23 @@
+"""Paged KV cache write and paged decode attention for AMD MI355X (gfx950).
+
+The work runs in hand-written HIP kernels behind the C ABI of ``libpkv.so``
+(``include/pkv.h``); this package is the thin ctypes binding over it.
+"""
+
+from ._binding import (  # noqa: F401
+    BF16,
+    EXPORTS,
+    F32,
+    LIB_PATH,
+    PkvError,
+    PoolDesc,
+    abi_version,
+    decode,
+    decode_partition,
+    decode_workspace_bytes,
+    load,
+    pool_desc,
+    prefill,
+    slot_mapping,
+    write,
+)

@@ -1,0 +1,245 @@
+"""ctypes binding of libpkv.so: argument marshalling only.
+
+Each function checks that the torch tensors it is handed have the shapes,
+dtypes, devices and layouts the kernels assume (the C ABI trusts its caller
+with buffer sizes), then passes raw device pointers and torch's current HIP
+stream to the library. There is no fallback: if the library is missing, or a
+call fails, an exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpkv.so")
+
+F32, BF16 = 0, 1
+_DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
+
+_STATUS = {0: "PKV_OK", 1: "PKV_ERR_NULL", 2: "PKV_ERR_DTYPE", 3: "PKV_ERR_SHAPE",
+           4: "PKV_ERR_UNSUPPORTED", 5: "PKV_ERR_WORKSPACE", 6: "PKV_ERR_HIP",
+           7: "PKV_ERR_ALIGN"}
+
+# Every symbol include/pkv.h declares.
+EXPORTS = ("pkv_slot_mapping", "pkv_write", "pkv_decode_partition",
+           "pkv_decode_workspace_bytes", "pkv_decode", "pkv_decode_partials",
+           "pkv_decode_reduce", "pkv_prefill", "pkv_status_string", "pkv_last_error",
+           "pkv_abi_version")
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        self.status_name = _STATUS.get(status, f"status {status}")
+        super().__init__(f"{self.status_name}: {message}")
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+
+
+def load(path: str | None = None):
+    """Load (once) and return the ctypes handle of libpkv.so."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is not built; run `python -m paged_kv_cache_scatter_amd.build` "
+                           "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(p)
+    lib.pkv_slot_mapping.argtypes = [_P, _I, _I, _P, _P, _I, _I, _I, _P, _P]
+    lib.pkv_slot_mapping.restype = ctypes.c_int
+    lib.pkv_write.argtypes = [_P, _P, _P, _I, _P, _P, ctypes.POINTER(PoolDesc), _P]
+    lib.pkv_write.restype = ctypes.c_int
+    lib.pkv_decode_partition.argtypes = [_I, _I, ctypes.POINTER(PoolDesc)]
+    lib.pkv_decode_partition.restype = _I
+    lib.pkv_decode_workspace_bytes.argtypes = [_I, _I, _I, _I, ctypes.POINTER(PoolDesc)]
+    lib.pkv_decode_workspace_bytes.restype = ctypes.c_size_t
+    dec_args = [_P, _I, _I, _P, _P, ctypes.POINTER(PoolDesc), _P, _I, _P, _I, ctypes.c_float,
+                _I, _P, _P, ctypes.c_size_t, _P]
+    for name in ("pkv_decode", "pkv_decode_partials", "pkv_decode_reduce"):
+        f = getattr(lib, name)
+        f.argtypes = dec_args
+        f.restype = ctypes.c_int
+    lib.pkv_prefill.argtypes = [_P, _P, _I, _I, _I, _I, _P, _P, ctypes.POINTER(PoolDesc), _P,
+                                _I, _P, _I, ctypes.c_float, _P, _P]
+    lib.pkv_prefill.restype = ctypes.c_int
+    lib.pkv_status_string.argtypes = [ctypes.c_int]
+    lib.pkv_status_string.restype = ctypes.c_char_p
+    lib.pkv_last_error.argtypes = []
+    lib.pkv_last_error.restype = ctypes.c_char_p
+    lib.pkv_abi_version.argtypes = []
+    lib.pkv_abi_version.restype = _I
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise PkvError(status, load().pkv_last_error().decode())
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
+    _need(isinstance(t, torch.Tensor), f"{name} must be a torch tensor")
+    _need(t.is_cuda, f"{name} must be on the GPU")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    if dtype is not None:
+        _need(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None:
+        _need(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)}, "
+              f"got {tuple(t.shape)}")
+
+
+def pool_desc(k_pool: torch.Tensor) -> PoolDesc:
+    _need(k_pool.dim() == 4, "pools are [num_blocks, block_size, num_kv_heads, head_dim]")
+    _need(k_pool.dtype in _DTYPES, f"pool dtype {k_pool.dtype} is not float32/bfloat16")
+    nb, bs, hkv, hd = k_pool.shape
+    return PoolDesc(nb, bs, hkv, hd, _DTYPES[k_pool.dtype])
+
+
+def _check_pools(k_pool, v_pool):
+    _dev(k_pool, "k_pool")
+    _dev(v_pool, "v_pool", dtype=k_pool.dtype, shape=k_pool.shape)
+    _need(k_pool.device == v_pool.device, "pools on different devices")
+    return pool_desc(k_pool)
+
+
+# ---------------------------------------------------------------- slot mapping
+def slot_mapping(tables: torch.Tensor, first_pos: torch.Tensor, cu_tokens: torch.Tensor,
+                 num_tokens: int, block_size: int, num_blocks: int,
+                 out: torch.Tensor | None = None) -> torch.Tensor:
+    """Flat slot of every token of a write (segments of consecutive positions)."""
+    _dev(tables, "tables", torch.int32)
+    _need(tables.dim() == 2, "tables must be [num_segments, max_blocks_per_seq]")
+    W, maxb = tables.shape
+    _dev(first_pos, "first_pos", torch.int32, (W,))
+    _dev(cu_tokens, "cu_tokens", torch.int32, (W + 1,))
+    if out is None:
+        out = torch.empty(int(num_tokens), dtype=torch.int32, device=tables.device)
+    _dev(out, "slot_mapping", torch.int32, (int(num_tokens),))
+    _check(load().pkv_slot_mapping(_ptr(tables), maxb, W, _ptr(first_pos), _ptr(cu_tokens),
+                                   int(num_tokens), int(block_size), int(num_blocks), _ptr(out),
+                                   _stream()))
+    return out
+
+
+# ---------------------------------------------------------------- write
+def write(k: torch.Tensor, v: torch.Tensor, slots: torch.Tensor, k_pool: torch.Tensor,
+          v_pool: torch.Tensor) -> None:
+    """Scatter rows of k, v ([T, Hkv, hd]) into the pools at ``slots`` ([T] int32)."""
+    desc = _check_pools(k_pool, v_pool)
+    _dev(slots, "slot_mapping", torch.int32)
+    _need(slots.dim() == 1, "slot_mapping must be 1-D")
+    T = slots.shape[0]
+    _dev(k, "k", k_pool.dtype, (T, desc.num_kv_heads, desc.head_dim))
+    _dev(v, "v", k_pool.dtype, (T, desc.num_kv_heads, desc.head_dim))
+    _check(load().pkv_write(_ptr(k), _ptr(v), _ptr(slots), T, _ptr(k_pool), _ptr(v_pool),
+                            ctypes.byref(desc), _stream()))
+
+
+# ---------------------------------------------------------------- decode
+def decode_partition(num_seqs: int, max_context_len: int, k_pool: torch.Tensor) -> int:
+    desc = pool_desc(k_pool)
+    return int(load().pkv_decode_partition(int(num_seqs), int(max_context_len),
+                                           ctypes.byref(desc)))
+
+
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, max_context_len: int,
+                           k_pool: torch.Tensor, partition: int = 0) -> int:
+    desc = pool_desc(k_pool)
+    return int(load().pkv_decode_workspace_bytes(int(num_seqs), int(num_q_heads),
+                                                 int(max_context_len), int(partition),
+                                                 ctypes.byref(desc)))
+
+
+def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+           block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+           max_context_len: int, out: torch.Tensor | None = None, partition: int = 0,
+           workspace: torch.Tensor | None = None, phase: str = "both") -> torch.Tensor:
+    """Paged decode attention; q [S, Hq, hd] -> out [S, Hq, hd].
+
+    ``max_context_len`` is a host-side bound on ``context_lens`` (the library
+    never reads device memory on the host). ``workspace`` is a uint8 device
+    tensor of at least ``decode_workspace_bytes(...)`` bytes (allocated here
+    if omitted and needed). ``phase``: "both", "partials" or "reduce".
+    """
+    desc = _check_pools(k_pool, v_pool)
+    _dev(q, "q", k_pool.dtype)
+    _need(q.dim() == 3 and q.shape[2] == desc.head_dim, "q must be [S, Hq, head_dim]")
+    S, Hq, _ = q.shape
+    _dev(block_tables, "block_tables", torch.int32)
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == S,
+          "block_tables must be [S, max_blocks_per_seq]")
+    maxb = block_tables.shape[1]
+    _dev(context_lens, "context_lens", torch.int32, (S,))
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype, q.shape)
+    need = decode_workspace_bytes(S, Hq, max_context_len, k_pool, partition)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace", torch.uint8)
+        ws_bytes = workspace.numel()
+    fn = {"both": "pkv_decode", "partials": "pkv_decode_partials",
+          "reduce": "pkv_decode_reduce"}[phase]
+    _check(getattr(load(), fn)(_ptr(q), S, Hq, _ptr(k_pool), _ptr(v_pool), ctypes.byref(desc),
+                               _ptr(block_tables), maxb, _ptr(context_lens),
+                               int(max_context_len), float(scale), int(partition), _ptr(out),
+                               _ptr(workspace), ws_bytes, _stream()))
+    return out
+
+
+# ---------------------------------------------------------------- prefill
+def prefill(q: torch.Tensor, cu_q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+            block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+            max_q_len: int, max_context_len: int,
+            out: torch.Tensor | None = None) -> torch.Tensor:
+    """Causal attention of packed query chunks q [sum n_s, Hq, hd] over the pool."""
+    desc = _check_pools(k_pool, v_pool)
+    _dev(q, "q", k_pool.dtype)
+    _need(q.dim() == 3 and q.shape[2] == desc.head_dim, "q must be [rows, Hq, head_dim]")
+    R, Hq, _ = q.shape
+    _dev(block_tables, "block_tables", torch.int32)
+    _need(block_tables.dim() == 2, "block_tables must be [S, max_blocks_per_seq]")
+    S, maxb = block_tables.shape
+    _dev(cu_q, "cu_q", torch.int32, (S + 1,))
+    _dev(context_lens, "context_lens", torch.int32, (S,))
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype, q.shape)
+    _check(load().pkv_prefill(_ptr(q), _ptr(cu_q), S, Hq, int(max_q_len), R, _ptr(k_pool),
+                              _ptr(v_pool), ctypes.byref(desc), _ptr(block_tables), maxb,
+                              _ptr(context_lens), int(max_context_len), float(scale), _ptr(out),
+                              _stream()))
+    return out
+
+
+def abi_version() -> int:
+    return int(load().pkv_abi_version())

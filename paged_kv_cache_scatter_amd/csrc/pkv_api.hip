@@ -1,0 +1,452 @@
+// Host entry points of the C ABI declared in include/pkv.h: argument checks,
+// work sizing and kernel launches on the caller's stream. No allocation, no
+// synchronisation, no device reads.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <cmath>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+
+namespace {
+thread_local char g_err[512] = "";
+
+constexpr int kMaxPartition = 8192;   // tokens per split (bounds the LDS table slice)
+constexpr int kMaxSplits = 4096;      // splits per sequence (bounds the merge kernel's LDS)
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+int ilog2(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int dtype_bytes(int dtype) { return dtype == PKV_F32 ? 4 : 2; }
+
+pkv_status check_pool(const pkv_pool_desc* pool) {
+  if (!pool) {
+    set_error("pool descriptor is NULL");
+    return PKV_ERR_NULL;
+  }
+  if (pool->dtype != PKV_F32 && pool->dtype != PKV_BF16) {
+    set_error("pool dtype %d is not PKV_F32 (0) or PKV_BF16 (1)", pool->dtype);
+    return PKV_ERR_DTYPE;
+  }
+  if (pool->num_blocks < 1 || pool->num_kv_heads < 1 || pool->head_dim < 1) {
+    set_error("pool sizes must be positive (num_blocks %d, num_kv_heads %d, head_dim %d)",
+              pool->num_blocks, pool->num_kv_heads, pool->head_dim);
+    return PKV_ERR_SHAPE;
+  }
+  if (!is_pow2(pool->block_size) || pool->block_size > 256) {
+    set_error("block_size %d must be a power of two in [1, 256]", pool->block_size);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if ((int64_t)pool->num_blocks * pool->block_size > INT32_MAX) {
+    set_error("num_blocks * block_size = %lld exceeds int32 slots",
+              (long long)pool->num_blocks * pool->block_size);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  return PKV_OK;
+}
+
+struct DecodePlan {
+  int rep = 0;
+  int partition = 0;
+  int splits = 0;
+  size_t ws_ml_bytes = 0;
+  size_t ws_bytes = 0;
+};
+
+int align_tokens(const pkv_pool_desc* pool) {
+  const int tile = decode_tile_tokens(pool->head_dim * dtype_bytes(pool->dtype));
+  return tile > pool->block_size ? tile : pool->block_size;
+}
+
+int auto_partition(int num_seqs, int max_ctx, const pkv_pool_desc* pool) {
+  const int align = align_tokens(pool);
+  if (max_ctx <= 0 || num_seqs <= 0) return align;
+  // Aim for about 8 split workgroups per CU, assuming lengths spread up to
+  // max_ctx (mean ~ max_ctx / 2): tokens per split ~ units * max_ctx / (16 * CUs).
+  const double units = (double)num_seqs * pool->num_kv_heads;
+  double p = units * (double)max_ctx / (16.0 * kNumCUs);
+  if (p < 256.0) p = 256.0;
+  int part = (int)std::ceil(p / align) * align;
+  const int cap = (kMaxPartition / align) * align;
+  if (part > cap) part = cap;
+  const int whole = ((max_ctx + align - 1) / align) * align;   // one split covers all
+  if (part > whole) part = whole;
+  if (part < align) part = align;
+  return part;
+}
+
+pkv_status plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
+                       int32_t max_ctx, int32_t partition, const pkv_pool_desc* pool,
+                       DecodePlan* plan) {
+  pkv_status st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0 || num_q_heads < 1 || max_ctx < 0 || max_blocks < 1) {
+    set_error("bad sizes: num_seqs %d, num_q_heads %d, max_context_len %d, "
+              "max_blocks_per_seq %d", num_seqs, num_q_heads, max_ctx, max_blocks);
+    return PKV_ERR_SHAPE;
+  }
+  if (num_q_heads % pool->num_kv_heads != 0) {
+    set_error("num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
+              pool->num_kv_heads);
+    return PKV_ERR_SHAPE;
+  }
+  if ((int64_t)max_ctx > (int64_t)max_blocks * pool->block_size) {
+    set_error("max_context_len %d exceeds max_blocks_per_seq * block_size = %lld", max_ctx,
+              (long long)max_blocks * pool->block_size);
+    return PKV_ERR_SHAPE;
+  }
+  const int rep = num_q_heads / pool->num_kv_heads;
+  if (!decode_supported(pool->dtype, pool->head_dim, rep)) {
+    set_error("head_dim %d with group size %d is not compiled (head_dim 16/32/64/128/256, "
+              "group 1..8)", pool->head_dim, rep);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  const int align = align_tokens(pool);
+  int part = partition;
+  if (part == 0) {
+    part = auto_partition(num_seqs, max_ctx, pool);
+  } else if (part < 0 || part % align != 0 || part > kMaxPartition) {
+    set_error("partition %d must be a positive multiple of %d and at most %d", part, align,
+              kMaxPartition);
+    return PKV_ERR_SHAPE;
+  }
+  const int splits = max_ctx > 0 ? (max_ctx + part - 1) / part : 1;
+  if (num_seqs > 65535 || splits > kMaxSplits) {
+    set_error("num_seqs %d exceeds 65535 or split count %d exceeds %d (raise partition)",
+              num_seqs, splits, kMaxSplits);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  plan->rep = rep;
+  plan->partition = part;
+  plan->splits = splits;
+  if (splits > 1) {
+    const size_t rows = (size_t)num_seqs * num_q_heads * splits;
+    plan->ws_ml_bytes = ((rows * 2 * sizeof(float)) + 255) & ~(size_t)255;
+    plan->ws_bytes = plan->ws_ml_bytes + rows * (size_t)pool->head_dim * sizeof(float);
+  }
+  return PKV_OK;
+}
+
+enum class Phase { kBoth, kPartials, kReduce };
+
+pkv_status decode_impl(Phase phase, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                       const void* k_pool, const void* v_pool, const pkv_pool_desc* pool,
+                       const int32_t* block_tables, int32_t max_blocks,
+                       const int32_t* context_lens, int32_t max_ctx, float scale,
+                       int32_t partition, void* out, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  DecodePlan plan;
+  pkv_status st = plan_decode(num_seqs, num_q_heads, max_blocks, max_ctx, partition, pool,
+                              &plan);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0) return PKV_OK;
+  if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out) {
+    set_error("NULL pointer among q %p, k_pool %p, v_pool %p, block_tables %p, "
+              "context_lens %p, out %p", q, k_pool, v_pool, (const void*)block_tables,
+              (const void*)context_lens, out);
+    return PKV_ERR_NULL;
+  }
+  if (!aligned16(q) || !aligned16(out) || !aligned16(k_pool) || !aligned16(v_pool)) {
+    set_error("q, out, k_pool and v_pool must be 16-byte aligned");
+    return PKV_ERR_ALIGN;
+  }
+  if (!std::isfinite(scale)) {
+    set_error("scale must be finite");
+    return PKV_ERR_SHAPE;
+  }
+  if (plan.ws_bytes > 0) {
+    if (!workspace) {
+      set_error("workspace is NULL but %zu bytes are needed", plan.ws_bytes);
+      return PKV_ERR_WORKSPACE;
+    }
+    if (workspace_bytes < plan.ws_bytes) {
+      set_error("workspace has %zu bytes, %zu needed", workspace_bytes, plan.ws_bytes);
+      return PKV_ERR_WORKSPACE;
+    }
+    if (!aligned16(workspace)) {
+      set_error("workspace must be 16-byte aligned");
+      return PKV_ERR_ALIGN;
+    }
+  }
+  DecodeArgs a;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.tables = block_tables;
+  a.ctx_lens = context_lens;
+  a.out = out;
+  a.ws_ml = plan.ws_bytes ? reinterpret_cast<float*>(workspace) : nullptr;
+  a.ws_o = plan.ws_bytes
+               ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + plan.ws_ml_bytes)
+               : nullptr;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.num_blocks = pool->num_blocks;
+  a.block_shift = ilog2(pool->block_size);
+  a.max_blocks = max_blocks;
+  a.max_ctx = max_ctx;
+  a.partition = plan.partition;
+  a.num_splits = plan.splits;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (phase != Phase::kReduce) {
+    st = launch_decode_partials(a, pool->dtype, pool->head_dim, plan.rep, s);
+    if (st != PKV_OK) return st;
+  }
+  if (phase != Phase::kPartials) {
+    st = launch_decode_reduce(a, pool->dtype, pool->head_dim, s);
+    if (st != PKV_OK) return st;
+  }
+  return PKV_OK;
+}
+
+}  // namespace
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+pkv_status launch_status(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("%s launch failed: %s", what, hipGetErrorString(e));
+    return PKV_ERR_HIP;
+  }
+  return PKV_OK;
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" {
+
+pkv_status pkv_slot_mapping(const int32_t* tables, int32_t max_blocks_per_seq,
+                            int32_t num_segments, const int32_t* first_pos,
+                            const int32_t* cu_tokens, int32_t num_tokens, int32_t block_size,
+                            int32_t num_blocks, int32_t* slot_mapping, void* stream) {
+  if (num_segments < 0 || num_tokens < 0 || max_blocks_per_seq < 1 || num_blocks < 1) {
+    set_error("bad sizes: num_segments %d, num_tokens %d, max_blocks_per_seq %d, "
+              "num_blocks %d", num_segments, num_tokens, max_blocks_per_seq, num_blocks);
+    return PKV_ERR_SHAPE;
+  }
+  if (!is_pow2(block_size) || block_size > 256) {
+    set_error("block_size %d must be a power of two in [1, 256]", block_size);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if ((int64_t)num_blocks * block_size > INT32_MAX) {
+    set_error("num_blocks * block_size exceeds int32 slots");
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (num_segments == 0 || num_tokens == 0) return PKV_OK;
+  if (!tables || !first_pos || !cu_tokens || !slot_mapping) {
+    set_error("NULL pointer among tables, first_pos, cu_tokens, slot_mapping");
+    return PKV_ERR_NULL;
+  }
+  SlotArgs a;
+  a.tables = tables;
+  a.first_pos = first_pos;
+  a.cu = cu_tokens;
+  a.slots = slot_mapping;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_segments = num_segments;
+  a.num_tokens = num_tokens;
+  a.block_shift = ilog2(block_size);
+  a.num_blocks = num_blocks;
+  launch_slot_mapping(a, reinterpret_cast<hipStream_t>(stream));
+  return launch_status("slot_mapping_kernel");
+}
+
+pkv_status pkv_write(const void* k, const void* v, const int32_t* slot_mapping,
+                     int32_t num_tokens, void* k_pool, void* v_pool, const pkv_pool_desc* pool,
+                     void* stream) {
+  pkv_status st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  if (num_tokens < 0) {
+    set_error("num_tokens %d is negative", num_tokens);
+    return PKV_ERR_SHAPE;
+  }
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !slot_mapping || !k_pool || !v_pool) {
+    set_error("NULL pointer among k %p, v %p, slot_mapping %p, k_pool %p, v_pool %p", k, v,
+              (const void*)slot_mapping, k_pool, v_pool);
+    return PKV_ERR_NULL;
+  }
+  const int isz = dtype_bytes(pool->dtype);
+  const int64_t row_bytes = (int64_t)pool->num_kv_heads * pool->head_dim * isz;
+  if (row_bytes > INT32_MAX / 2) {
+    set_error("row of %lld bytes is too large", (long long)row_bytes);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  const uintptr_t any = (uintptr_t)k | (uintptr_t)v | (uintptr_t)k_pool | (uintptr_t)v_pool;
+  if (any % (uintptr_t)isz) {
+    set_error("k, v, k_pool, v_pool must be aligned to the element size (%d)", isz);
+    return PKV_ERR_ALIGN;
+  }
+  const bool vec16 = (row_bytes % 16 == 0) && (any % 16 == 0);
+  WriteArgs a;
+  a.k = static_cast<const uint8_t*>(k);
+  a.v = static_cast<const uint8_t*>(v);
+  a.slots = slot_mapping;
+  a.k_pool = static_cast<uint8_t*>(k_pool);
+  a.v_pool = static_cast<uint8_t*>(v_pool);
+  a.pool_slots = (int64_t)pool->num_blocks * pool->block_size;
+  a.num_tokens = num_tokens;
+  a.row_bytes = (int32_t)row_bytes;
+  launch_write(a, vec16, isz, reinterpret_cast<hipStream_t>(stream));
+  return launch_status("write_kernel");
+}
+
+int32_t pkv_decode_partition(int32_t num_seqs, int32_t max_context_len,
+                             const pkv_pool_desc* pool) {
+  if (check_pool(pool) != PKV_OK) return 0;
+  return auto_partition(num_seqs, max_context_len, pool);
+}
+
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t max_context_len, int32_t partition,
+                                  const pkv_pool_desc* pool) {
+  if (!pool) return 0;
+  DecodePlan plan;
+  const int32_t maxb = pool->block_size > 0
+                           ? (max_context_len + pool->block_size - 1) / pool->block_size
+                           : 1;
+  if (plan_decode(num_seqs, num_q_heads, maxb > 0 ? maxb : 1, max_context_len, partition,
+                  pool, &plan) != PKV_OK)
+    return 0;
+  return plan.ws_bytes;
+}
+
+pkv_status pkv_decode(const void* q, int32_t num_seqs, int32_t num_q_heads, const void* k_pool,
+                      const void* v_pool, const pkv_pool_desc* pool,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t max_context_len, float scale,
+                      int32_t partition, void* out, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return decode_impl(Phase::kBoth, q, num_seqs, num_q_heads, k_pool, v_pool, pool, block_tables,
+                     max_blocks_per_seq, context_lens, max_context_len, scale, partition, out,
+                     workspace, workspace_bytes, stream);
+}
+
+pkv_status pkv_decode_partials(const void* q, int32_t num_seqs, int32_t num_q_heads,
+                               const void* k_pool, const void* v_pool,
+                               const pkv_pool_desc* pool, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                               int32_t max_context_len, float scale, int32_t partition,
+                               void* out, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return decode_impl(Phase::kPartials, q, num_seqs, num_q_heads, k_pool, v_pool, pool,
+                     block_tables, max_blocks_per_seq, context_lens, max_context_len, scale,
+                     partition, out, workspace, workspace_bytes, stream);
+}
+
+pkv_status pkv_decode_reduce(const void* q, int32_t num_seqs, int32_t num_q_heads,
+                             const void* k_pool, const void* v_pool, const pkv_pool_desc* pool,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t max_context_len, float scale,
+                             int32_t partition, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return decode_impl(Phase::kReduce, q, num_seqs, num_q_heads, k_pool, v_pool, pool,
+                     block_tables, max_blocks_per_seq, context_lens, max_context_len, scale,
+                     partition, out, workspace, workspace_bytes, stream);
+}
+
+pkv_status pkv_prefill(const void* q, const int32_t* cu_q, int32_t num_seqs, int32_t num_q_heads,
+                       int32_t max_q_len, int32_t total_q_rows, const void* k_pool,
+                       const void* v_pool, const pkv_pool_desc* pool,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* context_lens, int32_t max_context_len, float scale,
+                       void* out, void* stream) {
+  pkv_status st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0 || num_q_heads < 1 || max_q_len < 0 || total_q_rows < 0 ||
+      max_blocks_per_seq < 1 || max_context_len < 0) {
+    set_error("bad sizes: num_seqs %d, num_q_heads %d, max_q_len %d, total_q_rows %d, "
+              "max_blocks_per_seq %d, max_context_len %d", num_seqs, num_q_heads, max_q_len,
+              total_q_rows, max_blocks_per_seq, max_context_len);
+    return PKV_ERR_SHAPE;
+  }
+  if (num_q_heads % pool->num_kv_heads != 0) {
+    set_error("num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
+              pool->num_kv_heads);
+    return PKV_ERR_SHAPE;
+  }
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * pool->block_size) {
+    set_error("max_context_len %d exceeds max_blocks_per_seq * block_size", max_context_len);
+    return PKV_ERR_SHAPE;
+  }
+  const int rep = num_q_heads / pool->num_kv_heads;
+  if (!prefill_supported(pool->dtype, pool->head_dim, rep)) {
+    set_error("prefill: head_dim %d with group size %d is not compiled", pool->head_dim, rep);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (num_seqs == 0 || total_q_rows == 0 || max_q_len == 0) return PKV_OK;
+  if (!q || !cu_q || !k_pool || !v_pool || !block_tables || !context_lens || !out) {
+    set_error("NULL pointer among q, cu_q, k_pool, v_pool, block_tables, context_lens, out");
+    return PKV_ERR_NULL;
+  }
+  if (!aligned16(q) || !aligned16(out) || !aligned16(k_pool) || !aligned16(v_pool)) {
+    set_error("q, out, k_pool and v_pool must be 16-byte aligned");
+    return PKV_ERR_ALIGN;
+  }
+  if (!std::isfinite(scale)) {
+    set_error("scale must be finite");
+    return PKV_ERR_SHAPE;
+  }
+  if (num_seqs > 65535) {
+    set_error("num_seqs %d exceeds 65535", num_seqs);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  PrefillArgs a;
+  a.q = q;
+  a.cu_q = cu_q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.tables = block_tables;
+  a.ctx_lens = context_lens;
+  a.out = out;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.num_blocks = pool->num_blocks;
+  a.block_shift = ilog2(pool->block_size);
+  a.max_blocks = max_blocks_per_seq;
+  a.max_ctx = max_context_len;
+  a.max_q_len = max_q_len;
+  a.total_q = total_q_rows;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  return launch_prefill(a, pool->dtype, pool->head_dim, rep,
+                        reinterpret_cast<hipStream_t>(stream));
+}
+
+const char* pkv_status_string(pkv_status s) {
+  switch (s) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_ERR_NULL: return "PKV_ERR_NULL";
+    case PKV_ERR_DTYPE: return "PKV_ERR_DTYPE";
+    case PKV_ERR_SHAPE: return "PKV_ERR_SHAPE";
+    case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED";
+    case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE";
+    case PKV_ERR_HIP: return "PKV_ERR_HIP";
+    case PKV_ERR_ALIGN: return "PKV_ERR_ALIGN";
+  }
+  return "PKV_ERR_UNKNOWN";
+}
+
+const char* pkv_last_error(void) { return g_err; }
+
+int32_t pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+}  // extern "C"

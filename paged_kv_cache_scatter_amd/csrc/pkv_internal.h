@@ -1,0 +1,165 @@
+// Internal declarations shared by the host entry points and the kernel files.
+// Device helpers here are written for gfx950 (wave64, CDNA DPP controls).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pkv.h"
+
+namespace pkv {
+
+// ---------------------------------------------------------------- host side
+void set_error(const char* fmt, ...);   // records the thread-local message
+pkv_status launch_status(const char* what);  // hipGetLastError -> status
+
+constexpr int kNumCUs = 256;   // MI355X compute units (8 XCDs x 32)
+
+struct SlotArgs {
+  const int32_t* tables;
+  const int32_t* first_pos;
+  const int32_t* cu;
+  int32_t* slots;
+  int32_t max_blocks, num_segments, num_tokens, block_shift, num_blocks;
+};
+void launch_slot_mapping(const SlotArgs& a, hipStream_t st);
+
+struct WriteArgs {
+  const uint8_t* k;
+  const uint8_t* v;
+  const int32_t* slots;
+  uint8_t* k_pool;
+  uint8_t* v_pool;
+  int64_t pool_slots;
+  int32_t num_tokens;
+  int32_t row_bytes;
+};
+void launch_write(const WriteArgs& a, bool vec16, int elem_bytes, hipStream_t st);
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* tables;
+  const int32_t* ctx_lens;
+  void* out;
+  float* ws_ml;       // [S, Hq, J, 2]  (m in log2 units, l)
+  float* ws_o;        // [S, Hq, J, hd]
+  int32_t num_seqs, num_q_heads, num_kv_heads, num_blocks;
+  int32_t block_shift, max_blocks, max_ctx, partition, num_splits;
+  float scale_log2;   // scale * log2(e)
+};
+// Token tile per wave for a row of `row_bytes` (K or V of one KV head).
+int decode_tile_tokens(int row_bytes);
+// Returns false if (dtype, head_dim, rep) is not compiled.
+bool decode_supported(int dtype, int head_dim, int rep);
+pkv_status launch_decode_partials(const DecodeArgs& a, int dtype, int head_dim, int rep,
+                                  hipStream_t st);
+pkv_status launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim,
+                                hipStream_t st);
+
+struct PrefillArgs {
+  const void* q;
+  const int32_t* cu_q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* tables;
+  const int32_t* ctx_lens;
+  void* out;
+  int32_t num_seqs, num_q_heads, num_kv_heads, num_blocks;
+  int32_t block_shift, max_blocks, max_ctx, max_q_len, total_q;
+  float scale_log2;
+};
+bool prefill_supported(int dtype, int head_dim, int rep);
+pkv_status launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int rep,
+                          hipStream_t st);
+
+}  // namespace pkv
+
+// ---------------------------------------------------------------- device side
+namespace pkv {
+namespace dev {
+
+// DPP controls (GCN/CDNA encoding).
+constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+constexpr int kRowRor = 0x120;       // + n (1..15): rotate right within 16 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float swz_xor16(float x) {
+  // ds_swizzle bit mode: and_mask 0x1F, or_mask 0, xor_mask 0x10
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
+}
+
+__device__ __forceinline__ float xor32(float x) {
+  return __builtin_bit_cast(float, __shfl_xor(__builtin_bit_cast(int, x), 32));
+}
+
+// Sum over aligned groups of W consecutive lanes; every lane gets its group's sum.
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (W >= 2) x += dpp<kQuadXor1>(x);
+  if constexpr (W >= 4) x += dpp<kQuadXor2>(x);
+  if constexpr (W >= 8) x += dpp<kRowHalfMirror>(x);
+  if constexpr (W >= 16) x += dpp<kRowMirror>(x);
+  if constexpr (W >= 32) x += swz_xor16(x);
+  if constexpr (W >= 64) x += xor32(x);
+  return x;
+}
+
+// Sum over lanes that are congruent modulo STRIDE (STRIDE a power of two);
+// every lane gets the sum of its residue class.
+template <int STRIDE>
+__device__ __forceinline__ float strided_sum(float x) {
+  if constexpr (STRIDE <= 1) x += dpp<kRowRor + 1>(x);
+  if constexpr (STRIDE <= 2) x += dpp<kRowRor + 2>(x);
+  if constexpr (STRIDE <= 4) x += dpp<kRowRor + 4>(x);
+  if constexpr (STRIDE <= 8) x += dpp<kRowRor + 8>(x);
+  if constexpr (STRIDE <= 16) x += swz_xor16(x);
+  if constexpr (STRIDE <= 32) x += xor32(x);
+  return x;
+}
+
+// Max over aligned groups of W lanes (W in {1..64}); every lane gets the max.
+template <int W>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (W >= 2) x = fmaxf(x, dpp<kQuadXor1>(x));
+  if constexpr (W >= 4) x = fmaxf(x, dpp<kQuadXor2>(x));
+  if constexpr (W >= 8) x = fmaxf(x, dpp<kRowHalfMirror>(x));
+  if constexpr (W >= 16) x = fmaxf(x, dpp<kRowMirror>(x));
+  if constexpr (W >= 32) x = fmaxf(x, swz_xor16(x));
+  if constexpr (W >= 64) x = fmaxf(x, xor32(x));
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// bf16 bits <-> fp32
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) {
+  return __builtin_bit_cast(float, w & 0xFFFF0000u);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0x7FC0;  // NaN
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// a.lo*b.lo + a.hi*b.hi + c with bf16 pairs packed in 32-bit words, fp32 sum.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+}  // namespace dev
+}  // namespace pkv

@@ -1,0 +1,120 @@
+"""The C ABI without a GPU: the library loads, exports what include/pkv.h
+declares, and rejects bad arguments before touching the GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_scatter_amd as pkv
+from paged_kv_cache_scatter_amd._binding import PoolDesc
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "pkv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return pkv.load()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(pkv.EXPORTS) == names
+
+
+def test_abi_version_and_strings(lib):
+    assert lib.pkv_abi_version() == 1
+    for code, name in [(0, b"PKV_OK"), (3, b"PKV_ERR_SHAPE"), (7, b"PKV_ERR_ALIGN")]:
+        assert lib.pkv_status_string(code) == name
+
+
+def _desc(nb=64, bs=16, hkv=8, hd=128, dtype=1):
+    return PoolDesc(nb, bs, hkv, hd, dtype)
+
+
+def _dec(lib, desc, q=16, S=4, Hq=64, maxb=8, max_ctx=100, part=0, out=16, ws=None, wsb=0,
+         scale=0.1):
+    return lib.pkv_decode(q, S, Hq, 16, 16, ctypes.byref(desc), 16, maxb, 16, max_ctx, scale,
+                          part, out, ws, wsb, None)
+
+
+def _err(lib):
+    return lib.pkv_last_error().decode()
+
+
+def test_decode_argument_errors(lib):
+    d = _desc()
+    assert _dec(lib, _desc(dtype=5)) == 2 and "dtype" in _err(lib)
+    assert _dec(lib, d, Hq=60) == 3 and "multiple" in _err(lib)
+    assert _dec(lib, _desc(hd=96)) == 4 and "head_dim" in _err(lib)
+    assert _dec(lib, d, Hq=8 * 16) == 4              # group of 16 not compiled
+    assert _dec(lib, _desc(bs=12)) == 4 and "power of two" in _err(lib)
+    assert _dec(lib, d, max_ctx=200, maxb=8) == 3 and "max_context_len" in _err(lib)
+    assert _dec(lib, d, part=100) == 3 and "partition" in _err(lib)
+    assert _dec(lib, d, q=None) == 1 and "NULL" in _err(lib)
+    assert _dec(lib, d, q=8) == 7 and "aligned" in _err(lib)
+    assert _dec(lib, d, scale=float("inf")) == 3
+    # two splits of 64 tokens need a workspace
+    assert _dec(lib, d, part=64, max_ctx=100) == 5 and "workspace" in _err(lib)
+    need = lib.pkv_decode_workspace_bytes(4, 64, 100, 64, ctypes.byref(d))
+    assert _dec(lib, d, part=64, ws=16, wsb=need - 1) == 5
+    assert lib.pkv_decode(None, 0, 64, None, None, ctypes.byref(d), None, 8, None, 0, 1.0, 0,
+                          None, None, 0, None) == 0      # nothing to do
+
+
+def test_workspace_bytes(lib):
+    d = _desc(nb=32769, bs=16, hkv=8, hd=128)
+    # 64 sequences x 64 heads x 8 splits of 1024 tokens: (m, l) then o[128]
+    rows = 64 * 64 * 8
+    assert lib.pkv_decode_workspace_bytes(64, 64, 8192, 1024, ctypes.byref(d)) == \
+        rows * 2 * 4 + rows * 128 * 4
+    assert lib.pkv_decode_workspace_bytes(64, 64, 1024, 1024, ctypes.byref(d)) == 0
+    p = lib.pkv_decode_partition(64, 8192, ctypes.byref(d))
+    assert p > 0 and p % 32 == 0 and p % 16 == 0
+    # invalid arguments give 0 bytes
+    assert lib.pkv_decode_workspace_bytes(64, 60, 8192, 0, ctypes.byref(d)) == 0
+
+
+def test_write_and_slot_mapping_argument_errors(lib):
+    d = _desc()
+    assert lib.pkv_write(16, 16, 16, -1, 16, 16, ctypes.byref(d), None) == 3
+    assert lib.pkv_write(16, None, 16, 4, 16, 16, ctypes.byref(d), None) == 1
+    assert lib.pkv_write(16, 16, 16, 4, 16, 16, None, None) == 1
+    assert lib.pkv_write(16, 16, 16, 4, 16, 17, ctypes.byref(d), None) == 7
+    assert lib.pkv_write(16, 16, 16, 0, 16, 16, ctypes.byref(d), None) == 0
+    assert lib.pkv_write(16, 16, 16, 4, 16, 16, ctypes.byref(_desc(nb=1 << 28)), None) == 4
+    assert lib.pkv_slot_mapping(16, 4, 2, 16, 16, 8, 12, 64, 16, None) == 4   # bs 12
+    assert lib.pkv_slot_mapping(16, 0, 2, 16, 16, 8, 16, 64, 16, None) == 3
+    assert lib.pkv_slot_mapping(None, 4, 2, 16, 16, 8, 16, 64, 16, None) == 1
+    assert lib.pkv_slot_mapping(None, 4, 0, None, None, 0, 16, 64, None, None) == 0
+
+
+def test_prefill_argument_errors(lib):
+    d = _desc()
+    args = dict(q=16, cu=16, S=2, Hq=64, mq=8, tq=16)
+
+    def call(desc, **kw):
+        a = {**args, **kw}
+        return lib.pkv_prefill(a["q"], a["cu"], a["S"], a["Hq"], a["mq"], a["tq"], 16, 16,
+                               ctypes.byref(desc), 16, 8, 16, 100, 0.1, 16, None)
+    assert call(_desc(dtype=3)) == 2
+    assert call(d, Hq=63) == 3
+    assert call(d, S=-1) == 3
+
+
+def test_binding_checks_shapes_before_calling():
+    import torch
+    k = torch.zeros(2, 3)
+    with pytest.raises(ValueError):
+        pkv.write(k, k, torch.zeros(2, dtype=torch.int32), torch.zeros(1, 16, 1, 3),
+                  torch.zeros(1, 16, 1, 3))
