@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged decode step on one MI355X.
+
+One step = the whole path for one layer of a decode batch:
+  1. slot mapping of the new token of every sequence (position ctx - 1),
+  2. the KV write of those rows into the pool,
+  3. split-K paged decode attention over every sequence's whole context,
+  4. the merge of split partials.
+Default workload: the LLaMA-2-70B per-layer shape (64 sequences, context
+lengths log-uniform in [512, 8192), 64 query / 8 KV heads, head_dim 128,
+bf16, 16-token blocks scattered over a 32,769-block pool). The timed loop
+reads ~689 MB of K/V per step, well above the 256 MB Infinity Cache, so no
+input rotation is needed.
+
+Prints one JSON line: whole-step KV-read GB/s (`value`), the roofline of the
+dominant kernel (decode partials) from HIP events recorded around it in every
+timed step, and the CPU oracle timed on a bounded sample on the host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import paged_kv_cache_scatter_amd as pkv  # noqa: E402
+from workloads import CONFIGS, make_workload  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+DEV = torch.device("cuda:0")
+COUNTERS = os.path.join(ROOT, "profiles", "decode_partials_counters.json")
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(a).to(DEV)
+
+
+def workload_label(wl) -> str:
+    spec = CONFIGS[wl.cfg_id]
+    d = spec.ctx_dist
+    lens = {"uniform": f"U[{d[1]},{d[2]}]", "const": f"{d[1]}",
+            "loguniform": f"logU[{d[1]},{d[2]})"}[d[0]]
+    return (f"{wl.name}: {wl.num_seqs} seqs x ctx {lens}, {wl.num_q_heads} q / "
+            f"{wl.num_kv_heads} kv heads, head_dim {wl.head_dim}, block {wl.block_size}, "
+            f"pool {wl.num_blocks} blocks, {wl.dtype}")
+
+
+class Step:
+    """Device state for one decode step of workload ``wl``."""
+
+    def __init__(self, wl, partition: int = 0):
+        self.wl = wl
+        dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+        self.k_pool = torch.zeros(wl.pool_shape, dtype=dt, device=DEV)
+        self.v_pool = torch.zeros(wl.pool_shape, dtype=dt, device=DEV)
+        tabs, first, cu, rows = wl.bulk_segments(exclude_last=wl.prefix_tokens == 0)
+        n = int(cu[-1])
+        slots = pkv.slot_mapping(to_dev(tabs), to_dev(first), to_dev(cu), n, wl.block_size,
+                                 wl.num_blocks)
+        pkv.write(to_dev(wl.k_rows[rows]), to_dev(wl.v_rows[rows]), slots, self.k_pool,
+                  self.v_pool)
+        s_tabs, s_first, s_cu, s_rows = wl.step_segments()
+        self.s_tabs, self.s_first, self.s_cu = to_dev(s_tabs), to_dev(s_first), to_dev(s_cu)
+        self.n_new = int(s_cu[-1])
+        self.k_new, self.v_new = to_dev(wl.k_rows[s_rows]), to_dev(wl.v_rows[s_rows])
+        self.slots = torch.empty(self.n_new, dtype=torch.int32, device=DEV)
+        self.q = to_dev(wl.q)
+        self.out = torch.empty_like(self.q)
+        self.tables = to_dev(wl.block_tables)
+        self.ctx = to_dev(wl.context_lens)
+        self.max_ctx = int(wl.context_lens.max())
+        self.partition = partition or pkv.decode_partition(wl.num_seqs, self.max_ctx,
+                                                           self.k_pool)
+        nws = pkv.decode_workspace_bytes(wl.num_seqs, wl.num_q_heads, self.max_ctx,
+                                         self.k_pool, self.partition)
+        self.ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=DEV)
+        torch.cuda.synchronize()
+
+    def run(self, ev_a=None, ev_b=None):
+        wl = self.wl
+        pkv.slot_mapping(self.s_tabs, self.s_first, self.s_cu, self.n_new, wl.block_size,
+                         wl.num_blocks, out=self.slots)
+        pkv.write(self.k_new, self.v_new, self.slots, self.k_pool, self.v_pool)
+        if ev_a is not None:
+            ev_a.record()
+        pkv.decode(self.q, self.k_pool, self.v_pool, self.tables, self.ctx, wl.scale,
+                   self.max_ctx, out=self.out, partition=self.partition, workspace=self.ws,
+                   phase="partials")
+        if ev_b is not None:
+            ev_b.record()
+        pkv.decode(self.q, self.k_pool, self.v_pool, self.tables, self.ctx, wl.scale,
+                   self.max_ctx, out=self.out, partition=self.partition, workspace=self.ws,
+                   phase="reduce")
+
+
+def time_steps(step: Step, steps: int, warmup: int):
+    for _ in range(warmup):
+        step.run()
+    torch.cuda.synchronize()
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        step.run(ev_a[i], ev_b[i])
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    ms_kernel = float(np.mean([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]))
+    return ms_step, ms_kernel
+
+
+def time_decode_rotating(cfg: int, calls_per_set: int = 10):
+    """Decode-only timing (partials + merge) cycling over disjoint block sets of
+    one pool, so consecutive calls do not hit the Infinity Cache."""
+    wl = make_workload(cfg)
+    need = int(sum(-(-int(c) // wl.block_size) for c in wl.context_lens))
+    sets = max(1, min(24, (wl.num_blocks - 1) // need))
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    g = torch.Generator(device=DEV).manual_seed(7)
+    k_pool = torch.randn(wl.pool_shape, generator=g, device=DEV).to(dt)
+    v_pool = torch.randn(wl.pool_shape, generator=g, device=DEV).to(dt)
+    rng = np.random.default_rng(cfg)
+    perm = rng.permutation(wl.num_blocks - 1) + 1
+    tables = []
+    for r in range(sets):
+        ids = perm[r * need:(r + 1) * need]
+        t = np.zeros_like(wl.block_tables)
+        k = 0
+        for s in range(wl.num_seqs):
+            n = -(-int(wl.context_lens[s]) // wl.block_size)
+            t[s, :n] = ids[k:k + n]
+            k += n
+        tables.append(to_dev(t))
+    q, ctx = to_dev(wl.q), to_dev(wl.context_lens)
+    out = torch.empty_like(q)
+    max_ctx = int(wl.context_lens.max())
+    part = pkv.decode_partition(wl.num_seqs, max_ctx, k_pool)
+    ws = torch.empty(max(16, pkv.decode_workspace_bytes(wl.num_seqs, wl.num_q_heads, max_ctx,
+                                                        k_pool, part)),
+                     dtype=torch.uint8, device=DEV)
+
+    def call(tb):
+        pkv.decode(q, k_pool, v_pool, tb, ctx, wl.scale, max_ctx, out=out, partition=part,
+                   workspace=ws)
+
+    for r in range(sets * 2):
+        call(tables[r % sets])
+    torch.cuda.synchronize()
+    n = sets * calls_per_set
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for r in range(n):
+        call(tables[r % sets])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    kvb = wl.kv_bytes_per_call()
+    return {"workload": workload_label(wl), "partition": part, "rotating_sets": sets,
+            "us_per_call": round(ms * 1e3, 2), "kv_bytes": kvb,
+            "kv_read_GBps": round(kvb / (ms * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * kvb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+            "seq_steps_per_s": round(wl.num_seqs / (ms * 1e-3), 1)}
+
+
+def cpu_baseline(wl, budget_s: float = 12.0):
+    """The fp64 oracle on the host, on the first sequences of the same workload
+    until ``budget_s`` of CPU time is spent. The sample's blocks are renumbered
+    into a compact pool (the output does not depend on physical block ids)."""
+    import oracle  # test infrastructure: only this leg of the benchmark uses it
+
+    done_bytes, done_seqs, spent = 0, 0, 0.0
+    bs = wl.block_size
+    for s in range(wl.num_seqs):
+        L = int(wl.context_lens[s])
+        nb = -(-L // bs)
+        pool_shape = (nb + 1, bs, wl.num_kv_heads, wl.head_dim)
+        kp = np.zeros(pool_shape, wl.storage_np_dtype)
+        vp = np.zeros(pool_shape, wl.storage_np_dtype)
+        table = np.zeros((1, nb), np.int32)
+        table[0] = np.arange(1, nb + 1)
+        slots = oracle.slot_mapping(table, [0], [0, L], bs, nb + 1)
+        rows = wl.seq_rows[s]
+        kp, vp = oracle.write(kp, vp, wl.k_rows[rows], wl.v_rows[rows], slots)
+        t = time.perf_counter()
+        oracle.decode(wl.q[s:s + 1], kp, vp, table, wl.context_lens[s:s + 1], wl.scale,
+                      wl.dtype)
+        spent += time.perf_counter() - t
+        done_bytes += L * 2 * wl.num_kv_heads * wl.head_dim * wl.itemsize
+        done_seqs += 1
+        if spent >= budget_s:
+            break
+    ctx_tokens = int(wl.context_lens[:done_seqs].sum())
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"first {done_seqs} of {wl.num_seqs} sequences ({ctx_tokens} context "
+                      f"tokens, {done_bytes} KV bytes) of the same workload, fp64 numpy "
+                      f"oracle, single thread, {spent:.1f} s",
+            "seq_steps_per_s": round(done_seqs / spent, 3)}
+
+
+def traffic_from_counters(kernel_src: str):
+    """HBM bytes per launch measured by rocprofv3 counters, if they were taken on
+    the current kernel source; else None."""
+    if not os.path.exists(COUNTERS):
+        return None
+    with open(COUNTERS) as f:
+        c = json.load(f)
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    if c.get("kernel_source_sha256") != sha:
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=5, choices=sorted(CONFIGS))
+    ap.add_argument("--partition", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-extra", action="store_true", help="skip configs 3 and 4")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence or KV head with no exchange; see the design "
+              "notes)", file=sys.stderr)
+        sys.exit(2)
+    pkv.load()
+    print(f"[bench] generating config {args.config}", file=sys.stderr, flush=True)
+    wl = make_workload(args.config)
+    if wl.prefix_tokens:
+        raise SystemExit("the timed step needs a workload without a shared prefix")
+    step = Step(wl, args.partition)
+    print(f"[bench] timing {args.steps} steps (warmup {args.warmup}), partition "
+          f"{step.partition}", file=sys.stderr, flush=True)
+    ms_step, ms_kernel = time_steps(step, args.steps, args.warmup)
+    kvb = wl.kv_bytes_per_call()
+    gbs = kvb / (ms_step * 1e-3) / 1e9
+    achieved = kvb / (ms_kernel * 1e-3) / 1e9
+    src = os.path.join(ROOT, "paged_kv_cache_scatter_amd", "csrc", "pkv_decode.hip")
+    traffic = traffic_from_counters(src)
+    res = {
+        "metric": "paged decode attention: achieved KV-read GB/s and % HBM peak; seq-steps/s",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "accumulate": "fp32",
+        "data": "synthetic N(0,1) K/V/q at the model's per-layer shape, seeded",
+        "config": {"workload": workload_label(wl), "num_seqs": wl.num_seqs,
+                   "total_context_tokens": wl.total_ctx, "kv_bytes_per_step": kvb,
+                   "partition_tokens": step.partition,
+                   "step": "slot mapping + KV write of 1 token/seq + decode partials + merge"},
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "seq_steps_per_s": round(wl.num_seqs / (ms_step * 1e-3), 1),
+        "context_tokens_per_s": round(wl.total_ctx / (ms_step * 1e-3), 1),
+        "roofline": {"bound": "hbm", "kernel": "decode_partials_kernel",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel_ms": round(ms_kernel, 5),
+                     "algorithmic_bytes_per_launch": kvb},
+    }
+    if not args.no_extra:
+        extra = {}
+        for cfg in (3, 4):
+            if cfg == args.config:
+                continue
+            print(f"[bench] rotating decode timing, config {cfg}", file=sys.stderr, flush=True)
+            extra[f"config{cfg}"] = time_decode_rotating(cfg)
+        res["other_configs_decode_only"] = extra
+    if not args.no_cpu:
+        print("[bench] CPU oracle sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl)
+        res["cpu_baseline"]["host_cpu_count"] = os.cpu_count()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
