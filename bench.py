@@ -50,8 +50,12 @@ def to_dev(a: np.ndarray) -> torch.Tensor:
 def workload_label(wl) -> str:
     spec = CONFIGS[wl.cfg_id]
     d = spec.ctx_dist
-    lens = {"uniform": f"U[{d[1]},{d[2]}]", "const": f"{d[1]}",
-            "loguniform": f"logU[{d[1]},{d[2]})"}[d[0]]
+    if d[0] == "const":
+        lens = f"{d[1]}"
+    elif d[0] == "uniform":
+        lens = f"U[{d[1]},{d[2]}]"
+    else:
+        lens = f"logU[{d[1]},{d[2]})"
     return (f"{wl.name}: {wl.num_seqs} seqs x ctx {lens}, {wl.num_q_heads} q / "
             f"{wl.num_kv_heads} kv heads, head_dim {wl.head_dim}, block {wl.block_size}, "
             f"pool {wl.num_blocks} blocks, {wl.dtype}")
