@@ -206,6 +206,8 @@ pkv_status decode_impl(Phase phase, const void* q, int32_t num_seqs, int32_t num
   a.partition = plan.partition;
   a.num_splits = plan.splits;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.cu_q = nullptr;
+  a.total_q = 0;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (phase != Phase::kReduce) {
     st = launch_decode_partials(a, pool->dtype, pool->head_dim, plan.rep, s);

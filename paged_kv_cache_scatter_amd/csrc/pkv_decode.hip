@@ -572,18 +572,40 @@ decode_partials_kernel(DecodeArgs a) {
   using L = Lds<T, HD, REP>;
   extern __shared__ __align__(16) unsigned char smem[];
 
-  const int g = blockIdx.x, j = blockIdx.y, s = blockIdx.z;
+  const int g = blockIdx.x;
+  int j = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int hh = w % H::HS, stream = w / H::HS;             // head half, token stream
   const int bshift = a.block_shift;
   const int lim = min(a.max_ctx, a.max_blocks << bshift);
-  int ctx = a.ctx_lens[s];
-  ctx = ctx < 0 ? 0 : (ctx > lim ? lim : ctx);
+  int qrow = s;   // row of q and out
+  int ctx;
+  if (a.cu_q) {
+    // prefill row: its own causal context, one split
+    qrow = blockIdx.y * gridDim.z + blockIdx.z;
+    j = 0;
+    if (qrow >= a.total_q) return;
+    int lo = 0, hi = a.num_seqs;   // last sequence with cu_q[s] <= qrow
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.cu_q[mid] <= qrow) lo = mid;
+      else hi = mid;
+    }
+    s = lo;
+    int c = a.ctx_lens[s];
+    c = c < 0 ? 0 : (c > lim ? lim : c);
+    const int n = a.cu_q[s + 1] - a.cu_q[s];
+    ctx = c - n + (qrow - a.cu_q[s]) + 1;
+    ctx = ctx < 0 ? 0 : (ctx > lim ? lim : ctx);
+  } else {
+    ctx = a.ctx_lens[s];
+    ctx = ctx < 0 ? 0 : (ctx > lim ? lim : ctx);
+  }
   const int P = a.partition;
   const int nsplit = (ctx + P - 1) / P;
   const int hq0 = g * REP;
-  T* out = reinterpret_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + hq0) * HD;
+  T* out = reinterpret_cast<T*>(a.out) + ((size_t)qrow * a.num_q_heads + hq0) * HD;
 
   if (j >= nsplit) {
     if (j == 0) {  // empty sequence: zeros
@@ -618,7 +640,7 @@ decode_partials_kernel(DecodeArgs a) {
   const int kg = lane / G::LPT_K, kc = lane % G::LPT_K;
   const int vg = lane / G::LPT_V, vc = lane % G::LPT_V;
   const T* qp = reinterpret_cast<const T*>(a.q) +
-                ((size_t)s * a.num_q_heads + hq0 + hh * REPW) * HD;
+                ((size_t)qrow * a.num_q_heads + hq0 + hh * REPW) * HD;
   uint4 qr[REPW][G::KCH];
 #pragma unroll
   for (int h = 0; h < REPW; ++h)
@@ -784,6 +806,10 @@ pkv_status launch_split(const DecodeArgs& a, hipStream_t st) {
   const int tbl_entries = (a.partition >> a.block_shift) + 1;
   const int lds = Lds<T, HD, REP>::bytes(tbl_entries);
   dim3 grid(a.num_kv_heads, a.num_splits, a.num_seqs);
+  if (a.cu_q) {
+    const int z = a.total_q < kRowGridZ ? a.total_q : kRowGridZ;
+    grid = dim3(a.num_kv_heads, (a.total_q + z - 1) / z, z);
+  }
   hipLaunchKernelGGL((decode_partials_kernel<T, HD, REP>), grid, dim3(kThreads), lds, st, a);
   return launch_status("decode_partials_kernel");
 }

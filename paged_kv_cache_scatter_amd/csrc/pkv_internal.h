@@ -48,7 +48,12 @@ struct DecodeArgs {
   int32_t num_seqs, num_q_heads, num_kv_heads, num_blocks;
   int32_t block_shift, max_blocks, max_ctx, partition, num_splits;
   float scale_log2;   // scale * log2(e)
+  // Prefill rows: when cu_q is set, q/out hold total_q packed rows and row r of
+  // sequence s (n_s rows) attends positions 0 .. ctx_s - n_s + (r - cu_q[s]).
+  const int32_t* cu_q;
+  int32_t total_q;
 };
+constexpr int kRowGridZ = 32768;   // rows per grid z-extent in prefill-row launches
 // Token tile per wave for a row of `row_bytes` (K or V of one KV head).
 int decode_tile_tokens(int row_bytes);
 // Returns false if (dtype, head_dim, rep) is not compiled.
