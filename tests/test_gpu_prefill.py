@@ -8,7 +8,7 @@ import oracle
 import paged_kv_cache_scatter_amd as pkv
 from workloads import make_custom, make_workload
 
-from _gpu_util import DEV, PoolCase, check_close, note, out_f64, to_dev
+from _gpu_util import PoolCase, bits, check_close, note, out_f64, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -56,17 +56,136 @@ def test_prefill_chunks_small(dtype):
     assert not got[int(cu[3]):int(cu[3]) + 4].any(), "rows before position 0 are zero"
 
 
-def test_prefill_one_row_equals_decode():
+def _tables(lens, bs, rng, spare=3):
+    need = sum(-(-L // bs) for L in lens)
+    perm = (rng.permutation(need + spare) + 1).tolist()
+    tabs, k = [], 0
+    for L in lens:
+        n = -(-L // bs)
+        tabs.append(perm[k:k + n])
+        k += n
+    return tabs, need + spare + 1
+
+
+def _case(lens, qlens, dtype, hd, rep, hkv=2, bs=16, seed=0, fill="nan"):
+    rng = np.random.default_rng(seed)
+    tabs, nb = _tables(lens, bs, rng)
+    wl = make_custom(tabs, lens, dtype=dtype, num_q_heads=hkv * rep, num_kv_heads=hkv,
+                     head_dim=hd, block_size=bs, num_blocks=nb, seed=seed)
+    pc = PoolCase(wl, fill=fill)
+    cu = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    q_rows = _rand_rows(int(cu[-1]), wl, seed + 100)
+    return pc, cu, q_rows
+
+
+def _ref(pc, q_rows, cu, tables=None, ctx=None):
+    wl = pc.wl
+    kp, vp = pc.ref_pools()
+    return oracle.prefill(q_rows, cu, kp, vp, wl.block_tables if tables is None else tables,
+                          wl.context_lens if ctx is None else ctx, wl.scale, wl.dtype)
+
+
+@pytest.mark.parametrize("hd", [64, 128])
+def test_prefill_matrix_core_variants(hd):
+    """bf16 chunks on every compiled group size: chunks spanning several query
+    tiles with ragged ends, a one-row chunk, and a chunk longer than its
+    context (leading rows zero); K/V ranges spanning several key tiles."""
+    lens = [150, 70, 33, 300, 1]
+    qlens = [150, 20, 40, 130, 1]
+    for rep in range(1, 9):
+        pc, cu, q_rows = _case(lens, qlens, "bf16", hd, rep, seed=rep)
+        got = out_f64(_run(pc, q_rows, cu, max(qlens)), "bf16")
+        check_close(got, _ref(pc, q_rows, cu), "bf16", f"hd={hd} rep={rep}")
+        z0 = int(cu[2])
+        assert not got[z0:z0 + 7].any(), "rows before position 0 are zero"
+
+
+@pytest.mark.parametrize("bs", [1, 8, 32, 64])
+def test_prefill_block_sizes(bs):
+    lens = [3, 70, 129, 260]
+    qlens = [3, 70, 50, 200]
+    pc, cu, q_rows = _case(lens, qlens, "bf16", 128, 4, bs=bs, seed=bs)
+    got = out_f64(_run(pc, q_rows, cu, max(qlens)), "bf16")
+    check_close(got, _ref(pc, q_rows, cu), "bf16", f"bs={bs}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_poison_is_bitwise_invisible(dtype):
+    """Slots no token was written to (zero, NaN or huge values) never reach
+    the output: identical bits for all three fills."""
+    lens = [17, 64, 100, 333]
+    qlens = [17, 30, 100, 77]
+    outs = []
+    for fill in ("zero", "nan", "huge"):
+        pc, cu, q_rows = _case(lens, qlens, dtype, 64, 4, seed=21, fill=fill)
+        outs.append(to_host(_run(pc, q_rows, cu, max(qlens))))
+    assert np.array_equal(bits(outs[1]), bits(outs[0]))
+    assert np.array_equal(bits(outs[2]), bits(outs[0]))
+    check_close(oracle.storage_to_f64(outs[1], dtype), _ref(pc, q_rows, cu), dtype)
+
+
+def test_prefill_invalid_block_id_is_excluded():
+    lens = [100, 64]
+    qlens = [60, 64]
+    pc, cu, q_rows = _case(lens, qlens, "bf16", 128, 8, seed=31)
+    bad = pc.wl.block_tables.copy()
+    bad[0, 2] = 1 << 20
+    bad[1, 0] = -3
+    note("prefill with out-of-range block ids")
+    wl = pc.wl
+    out = pkv.prefill(to_dev(q_rows), to_dev(cu), pc.k_pool, pc.v_pool, to_dev(bad), pc.ctx,
+                      wl.scale, max(qlens), pc.max_ctx)
+    torch.cuda.synchronize()
+    check_close(out_f64(out, "bf16"), _ref(pc, q_rows, cu, tables=bad), "bf16")
+
+
+def test_prefill_context_beyond_max_context_len_is_clamped():
+    lens = [200, 90]
+    qlens = [40, 40]
+    pc, cu, q_rows = _case(lens, qlens, "bf16", 64, 2, seed=41)
+    wl = pc.wl
+    note("prefill with max_context_len below the real lengths")
+    out = pkv.prefill(to_dev(q_rows), to_dev(cu), pc.k_pool, pc.v_pool, pc.tables, pc.ctx,
+                      wl.scale, max(qlens), 120)
+    torch.cuda.synchronize()
+    ctx = np.minimum(wl.context_lens, 120).astype(np.int32)
+    check_close(out_f64(out, "bf16"), _ref(pc, q_rows, cu, ctx=ctx), "bf16")
+
+
+def test_prefill_long_table_takes_row_path():
+    """Block size 1 with a 2,100-token context: more table entries than the
+    matrix-core path stages, so the row path runs; same results."""
+    lens = [2100, 40]
+    qlens = [24, 40]
+    pc, cu, q_rows = _case(lens, qlens, "bf16", 64, 2, bs=1, seed=51)
+    got = out_f64(_run(pc, q_rows, cu, max(qlens)), "bf16")
+    check_close(got, _ref(pc, q_rows, cu), "bf16", "bs=1 long table")
+
+
+def test_prefill_one_row_equals_decode_row_path():
     """A one-row chunk at each sequence's last position is that sequence's
-    decode step; with the same single split the bits are identical."""
-    wl = make_workload(5, num_seqs=3)
+    decode step. fp32 prefill runs the decode kernel's row mode, so with the
+    same single split the bits are identical."""
+    wl = make_workload(2, num_seqs=5)
     pc = PoolCase(wl)
-    cu = np.arange(4, dtype=np.int32)
+    cu = np.arange(wl.num_seqs + 1, dtype=np.int32)
     got = _run(pc, wl.q, cu, 1)
     whole = -(-pc.max_ctx // 16) * 16
     dec = pc.decode(partition=whole)
-    assert torch.equal(got.view(torch.int16), dec.view(torch.int16))
-    check_close(out_f64(got, "bf16"), pc.ref_decode(), "bf16")
+    assert torch.equal(got.view(torch.int32), dec.view(torch.int32))
+    check_close(out_f64(got, "f32"), pc.ref_decode(), "f32")
+
+
+def test_prefill_one_row_matches_decode_matrix_cores():
+    """The same on config 5's shapes (bf16, matrix-core path): both agree with
+    the oracle's decode."""
+    wl = make_workload(5, num_seqs=3)
+    pc = PoolCase(wl)
+    cu = np.arange(4, dtype=np.int32)
+    got = out_f64(_run(pc, wl.q, cu, 1), "bf16")
+    ref = pc.ref_decode()
+    check_close(got, ref, "bf16", "prefill")
+    check_close(out_f64(pc.decode(), "bf16"), ref, "bf16", "decode")
 
 
 def test_prefill_config5_variant_sampled():
