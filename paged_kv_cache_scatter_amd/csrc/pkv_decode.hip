@@ -9,23 +9,28 @@
 // pages gather a contiguous copy first; here the blocks are read where they lie.
 //
 // Work decomposition: one workgroup (4 waves) per (KV head g, split j,
-// sequence s). The split's slice of the block table is staged in LDS once.
-// Each wave takes token tiles of TILE tokens in turn (tiles w, w+4, ...):
-//   K stage   lanes own (token, two 16-byte chunks of its K row); the REP query
+// sequence s). Each wave takes token tiles of TILE tokens in turn (tiles w,
+// w+4, ...) and streams them into its own two-stage LDS ring with 16-byte
+// direct-to-LDS loads, one tile ahead of the one it computes. When a load
+// instruction's 64 lanes stay inside one block (tokens per instruction <=
+// block size), the tile's block ids are scalar loads issued a tile ahead and
+// every row address is one scalar base plus a fixed lane offset; otherwise the
+// split's ids are staged in LDS first. Tokens past the split or in an invalid
+// block are read from a zero row and get a -inf score, so every tile, the
+// partial last one included, goes through the same pipelined ring.
+//   K stage   lanes own (token, KCH 16-byte chunks of its K row); the REP query
 //             heads of the group sit in registers, so each K row is read once
 //             for the whole group. The partial dot products of a token are
 //             combined across its lanes by a DPP reduce-scatter that leaves each
 //             lane holding the complete score of one head (or a few).
 //   softmax   each lane runs the online max/sum for its own head(s) over its
 //             tokens; a strided DPP max joins the lanes of one head. Every exp
-//             is computed once. Probabilities go to a small LDS tile.
-//   V stage   lanes own (token, one 16-byte chunk of its V row); probabilities
-//             are broadcast reads from LDS; o[REP][chunk] accumulates in fp32.
-//             The rescale of o is skipped when no head's running max moved.
-// Loads are software-pipelined across tiles: the next tile's K rows are issued
-// as soon as this tile's scores are formed, its V rows as soon as this tile's
-// V has been consumed. Only the split's last partial tile (or a split with an
-// invalid table entry) takes the masked, unpipelined path.
+//             is computed once. Probabilities go to a small LDS tile (bf16: a
+//             rounded pair of tokens per word).
+//   V stage   each lane owns DPL output dims of HPV heads for the whole tile and
+//             reads the V rows from the ring (all lanes of a head set read one
+//             row contiguously); o accumulates in fp32 and needs no cross-lane
+//             reduction. The rescale of o is skipped when no running max moved.
 // At the end the four waves' (m, l, o) are merged in LDS and either the
 // normalised output (single split) or the split partial is written.
 #include "pkv_internal.h"
@@ -46,18 +51,26 @@ constexpr int pow2ceil(int x) {
   return p;
 }
 
+// Largest power of two p with p * p <= x (1 for x < 4).
+constexpr int isqrt_p2(int x) {
+  int p = 1;
+  while (4 * p * p <= x) p <<= 1;
+  return p;
+}
+
 template <typename T, int HD, int REP>
 struct Geo {
   static constexpr int ISZ = (int)sizeof(T);
   static constexpr int ROWB = HD * ISZ;  // bytes of one K (or V) row of one KV head
   static constexpr int EPC = 16 / ISZ;   // elements per 16-byte chunk
-  // tokens per tile: 8 KB of K plus V per wave and tile (at most 64 tokens)
-  static constexpr int TILE = ROWB >= 1024 ? 4 : ROWB >= 512 ? 8 : ROWB >= 256 ? 16 : ROWB >= 128 ? 32 : 64;
+  // tokens per tile: 4 KB of K plus V per wave and tile for rows of 256 bytes
+  // or more, 8 KB for shorter rows (at most 64 tokens)
+  static constexpr int TILE = ROWB >= 1024 ? 2 : ROWB >= 512 ? 4 : ROWB >= 256 ? 8 : ROWB >= 128 ? 32 : 64;
   static constexpr int KCH = ROWB >= 32 ? 2 : 1;    // K chunks per lane per row
   static constexpr int LPT_K = ROWB / (16 * KCH);   // lanes per token (K stage)
   static constexpr int TPW_K = 64 / LPT_K;          // tokens per wave load (K)
   static constexpr int RK = TILE / TPW_K;           // K rows per lane per tile
-  static constexpr int LPT_V = ROWB / 16;           // lanes per token (V stage)
+  static constexpr int LPT_V = ROWB / 16;           // lanes per token (V loads)
   static constexpr int TPW_V = 64 / LPT_V;
   static constexpr int RV = TILE / TPW_V;           // V rows per lane per tile
   // heads after the reduce-scatter of the K stage
@@ -65,7 +78,23 @@ struct Geo {
   static constexpr int RS = REPP < LPT_K ? REPP : LPT_K;   // lanes one head set spreads over
   static constexpr int HPL = REPP / RS;             // heads per lane
   static constexpr int DUP = LPT_K / RS;            // lanes holding the same heads
+  // V stage: lane owns DPL dims of HPV heads. DPL near sqrt(REP * HD / 64)
+  // balances the probability words and the V bytes each lane reads per tile.
+  static constexpr int DPL_MIN = HD / 64 > 2 ? HD / 64 : 2;
+  static constexpr int DPL = isqrt_p2(REP * HD / 64) > DPL_MIN ? isqrt_p2(REP * HD / 64) : DPL_MIN;
+  static constexpr int LPH = HD / DPL;              // lanes per head set
+  static constexpr int HG = 64 / LPH;               // head sets across the wave
+  static constexpr int HPV = (REP + HG - 1) / HG;   // heads per lane
+  static constexpr int PSTR = REPP > HG * HPV ? REPP : HG * HPV;   // probability row stride
+  static constexpr int PROWS = ISZ == 2 ? TILE / 2 : TILE;          // probability rows
+  // ring stage: RK*KCH K loads then RV V loads, 1 KB per wave each
+  static constexpr int LOADS = RK * KCH + RV;
+  static constexpr int STAGE = LOADS * 1024;
+  static constexpr int VOFF = RK * KCH * 1024;      // V rows (token-major) in a stage
+  static constexpr int NID = TILE / (TPW_K > TPW_V ? TPW_K : TPW_V);   // block ids per tile
+  static constexpr int STAGES = 2;                  // tiles in a wave's LDS ring
   static_assert(RK >= 1 && RV >= 1 && LPT_K >= 1 && LPT_K <= 32 && LPT_V <= 64, "geometry");
+  static_assert(LPH >= 1 && LPH <= 64 && DPL * ISZ <= 16 && (ISZ == 4 || TILE % 2 == 0), "PV");
 };
 
 __device__ __forceinline__ uint4 ld16(const char* p) {
@@ -190,9 +219,9 @@ __device__ __forceinline__ float strided_reduce(float x) {
 template <typename T, int HD, int REP>
 struct WaveState {
   using G = Geo<T, HD, REP>;
-  float m[G::HPL];          // running max (log2 units) of the lane's heads
-  float lsum[G::HPL];       // this lane's share of the exp-sum of its heads
-  float o[REP][G::EPC];     // unnormalised output chunk (V-stage layout)
+  float m[G::HPL];          // running max (log2 units) of the lane's K-stage heads
+  float lsum[G::HPL];       // this lane's share of the exp-sum of those heads
+  float o[G::HPV][G::DPL];  // unnormalised output: DPL dims of HPV heads (PV layout)
 };
 
 struct SplitCtx {
@@ -200,105 +229,84 @@ struct SplitCtx {
   const char* vb;     // lane base into v_pool: + g*HD*isz + vc*16
   const char* kh;     // head base into k_pool: + g*HD*isz (uniform)
   const char* vh;     // head base into v_pool: + g*HD*isz (uniform)
+  const char* kz;     // lane's K chunk in the zero row
+  const char* vz;     // lane's V chunk in the zero row
   uint32_t koff;      // lane offset of its K chunk within a row group: kg*rsb + kc*16
   uint32_t voff;      // lane offset of its V chunk within a row group: vg*rsb + vc*16
-  const int* tbl;     // LDS block ids of this split (-1 = invalid)
+  const int* trow;    // this sequence's block table row (global)
+  const int* tbl;     // LDS block ids of this split (-1 = invalid); per-lane path only
   int tbl_base;       // logical block index of tbl[0]
   int bshift;
+  int num_blocks;
   uint32_t blk_bytes; // bytes of one block of one pool (all heads)
   uint32_t rsb;       // bytes of one token row (all heads)
   int t1;             // end of the split (exclusive)
   float scale_log2;
 };
 
-template <typename T, int HD, int REP, bool MASKED>
-__device__ __forceinline__ void load_k(const SplitCtx& c, int tb, int kg,
-                                       uint4 (&kr)[Geo<T, HD, REP>::RK][Geo<T, HD, REP>::KCH],
-                                       bool (&kval)[Geo<T, HD, REP>::RK]) {
-  using G = Geo<T, HD, REP>;
-  const int bmask = (1 << c.bshift) - 1;
+// Block ids of one tile on the uniform path (every 16-byte load instruction of
+// the wave stays inside one block): one id per block the tile touches. ok bit
+// i: id[i] is a valid block.
+template <int NID>
+struct TileIds {
+  int id[NID];
+  uint32_t ok;
+  bool masked;        // partial tile or an invalid id: zero rows and -inf scores
+};
+
+template <int NID>
+__device__ __forceinline__ int pick(const TileIds<NID>& ti, int i) {
+  int v = ti.id[0];
 #pragma unroll
-  for (int r = 0; r < G::RK; ++r) {
-    const int t = tb + r * G::TPW_K + kg;
-    bool ok = true;
-    int blk;
-    if (MASKED) {
-      blk = t < c.t1 ? c.tbl[(t >> c.bshift) - c.tbl_base] : -1;
-      ok = blk >= 0;
-      blk = ok ? blk : 0;
-    } else {
-      blk = c.tbl[(t >> c.bshift) - c.tbl_base];
-    }
-    kval[r] = ok;
-    const char* p = c.kb + (uint64_t)(uint32_t)blk * c.blk_bytes +
-                    (uint32_t)(t & bmask) * c.rsb;
-#pragma unroll
-    for (int i = 0; i < G::KCH; ++i) {
-      if (MASKED) {
-        kr[r][i] = make_uint4(0, 0, 0, 0);
-        if (ok) kr[r][i] = ld16(p + i * G::LPT_K * 16);
-      } else {
-        kr[r][i] = ld16(p + i * G::LPT_K * 16);
-      }
-    }
-  }
+  for (int k = 1; k < NID; ++k) v = i == k ? ti.id[k] : v;
+  return v;
 }
 
-template <typename T, int HD, int REP, bool MASKED>
-__device__ __forceinline__ void load_v(const SplitCtx& c, int tb, int vg,
-                                       uint4 (&vr)[Geo<T, HD, REP>::RV]) {
+// Block ids on the uniform path are copied from the table into LDS in batches
+// of 64 entries (TPB tiles of NID entries), one direct-to-LDS word per lane,
+// into one of two batch slots. A batch is requested when the first tile of the
+// previous one is issued, so it retires long before it is read, in order with
+// the tile loads.
+template <typename T, int HD, int REP>
+__device__ __forceinline__ void ids_batch_dma(const SplitCtx& c, int tb0, int step, int n,
+                                              int b, int lane, uint32_t slots) {
   using G = Geo<T, HD, REP>;
-  const int bmask = (1 << c.bshift) - 1;
-#pragma unroll
-  for (int r = 0; r < G::RV; ++r) {
-    const int t = tb + r * G::TPW_V + vg;
-    bool ok = true;
-    int blk;
-    if (MASKED) {
-      blk = t < c.t1 ? c.tbl[(t >> c.bshift) - c.tbl_base] : -1;
-      ok = blk >= 0;
-      blk = ok ? blk : 0;
-    } else {
-      blk = c.tbl[(t >> c.bshift) - c.tbl_base];
-    }
-    const char* p = c.vb + (uint64_t)(uint32_t)blk * c.blk_bytes +
-                    (uint32_t)(t & bmask) * c.rsb;
-    if (MASKED) {
-      vr[r] = make_uint4(0, 0, 0, 0);
-      if (ok) vr[r] = ld16(p);
-    } else {
-      vr[r] = ld16(p);
-    }
-  }
-}
-
-// Full tiles when a wave's load row never straddles a block (tokens per wave
-// load <= block size): the row's block id is one wave-uniform value, read once
-// from LDS into a scalar register, and each lane only adds its fixed offset.
-__device__ __forceinline__ const char* row_base(const SplitCtx& c, const char* head, int t) {
-  const int blk = __builtin_amdgcn_readfirstlane(c.tbl[(t >> c.bshift) - c.tbl_base]);
-  const uint32_t in_blk = (uint32_t)(t & ((1 << c.bshift) - 1));
-  return head + (uint64_t)(uint32_t)blk * c.blk_bytes + in_blk * c.rsb;
+  constexpr int TPB = 64 / G::NID;
+  const int m = min(b * TPB + lane / G::NID, n - 1);   // this lane's tile
+  const int tb = tb0 + m * step;
+  const int fb = tb >> c.bshift;
+  const int lb = (min(tb + G::TILE, c.t1) - 1) >> c.bshift;   // last block with a live token
+  dma4(c.trow + min(fb + lane % G::NID, lb), slots + (b & 1) * 256);
 }
 
 template <typename T, int HD, int REP>
-__device__ __forceinline__ void load_k_uni(const SplitCtx& c, int tb,
-                                           uint4 (&kr)[Geo<T, HD, REP>::RK][Geo<T, HD, REP>::KCH]) {
+__device__ __forceinline__ TileIds<Geo<T, HD, REP>::NID> read_ids(const SplitCtx& c, int tb, int m,
+                                                                 const int* slots) {
   using G = Geo<T, HD, REP>;
+  constexpr int TPB = 64 / G::NID;
+  const int* e = slots + ((m / TPB) & 1) * 64 + (m % TPB) * G::NID;
+  TileIds<G::NID> ti;
+  const int fb = tb >> c.bshift;
+  const int lb = (min(tb + G::TILE, c.t1) - 1) >> c.bshift;
+  ti.ok = 0;
 #pragma unroll
-  for (int r = 0; r < G::RK; ++r) {
-    const char* base = row_base(c, c.kh, tb + r * G::TPW_K);
-#pragma unroll
-    for (int i = 0; i < G::KCH; ++i) kr[r][i] = ld16(base + c.koff + i * G::LPT_K * 16);
+  for (int i = 0; i < G::NID; ++i) {
+    const int id = __builtin_amdgcn_readfirstlane(e[i]);
+    const bool ok = fb + i <= lb && (unsigned)id < (unsigned)c.num_blocks;
+    ti.id[i] = ok ? id : 0;
+    ti.ok |= (uint32_t)ok << i;
   }
+  ti.masked = tb + G::TILE > c.t1 || ti.ok != (2u << (lb - fb)) - 1u;
+  return ti;
 }
 
-template <typename T, int HD, int REP>
-__device__ __forceinline__ void load_v_uni(const SplitCtx& c, int tb,
-                                           uint4 (&vr)[Geo<T, HD, REP>::RV]) {
-  using G = Geo<T, HD, REP>;
-#pragma unroll
-  for (int r = 0; r < G::RV; ++r) vr[r] = ld16(row_base(c, c.vh, tb + r * G::TPW_V) + c.voff);
+// Token tt of a tile starting at tb is live: inside the split and in a valid block.
+template <typename T, int HD, int REP, bool UNI>
+__device__ __forceinline__ bool live(const SplitCtx& c, const TileIds<Geo<T, HD, REP>::NID>& ti,
+                                     int tb, int tt) {
+  if (tt >= c.t1) return false;
+  if (UNI) return (ti.ok >> ((tt - tb) >> c.bshift)) & 1u;
+  return c.tbl[(tt >> c.bshift) - c.tbl_base] >= 0;
 }
 
 // Scores of the tile's K rows (log2 units), reduce-scattered to the lane's heads.
@@ -330,13 +338,14 @@ __device__ __forceinline__ void tile_scores(
   }
 }
 
-// Online softmax of the lane's heads over the tile; writes probabilities (and,
-// when some running max moved, the rescale factors) to the wave's LDS tile.
-// Returns whether any head's running max moved in this wave.
+// Online softmax of the lane's heads over the tile. Probabilities go to the
+// wave's LDS tile: bf16 as a pair (token 2i, token 2i+1) rounded and packed
+// in one word per head, fp32 one float per (token, head); the rescale factors
+// go to cbuf when some running max moved. Returns whether one moved.
 template <typename T, int HD, int REP>
 __device__ __forceinline__ bool tile_softmax(
     WaveState<T, HD, REP>& st, const float (&sc)[Geo<T, HD, REP>::RK][Geo<T, HD, REP>::HPL],
-    int kg, int hb, bool dup0, float* pbuf, float* cbuf) {
+    int kg, int hb, bool dup0, uint32_t* pbuf, float* cbuf) {
   using G = Geo<T, HD, REP>;
   bool moved = false;
   float corr[G::HPL];
@@ -358,7 +367,13 @@ __device__ __forceinline__ bool tile_softmax(
     for (int r = 0; r < G::RK; ++r) {
       const float p = fast_exp2(sc[r][j] - mref);
       ps += p;
-      if (dup0 && h < REP) pbuf[(r * G::TPW_K + kg) * G::REPP + h] = p;
+      const int tt = r * G::TPW_K + kg;
+      if constexpr (G::ISZ == 2) {
+        const float pn = __shfl_xor(p, G::LPT_K);   // same head, token tt ^ 1
+        if (dup0 && h < REP && !(kg & 1)) pbuf[(tt >> 1) * G::PSTR + h] = pack_bf16x2(p, pn);
+      } else {
+        if (dup0 && h < REP) reinterpret_cast<float*>(pbuf)[tt * G::PSTR + h] = p;
+      }
     }
     st.lsum[j] = fmaf(st.lsum[j], corr[j], dup0 ? ps : 0.f);
   }
@@ -373,193 +388,289 @@ __device__ __forceinline__ bool tile_softmax(
   return any_moved;
 }
 
+// N consecutive 32-bit words from LDS, in the widest aligned pieces.
+template <int N, int STR>
+__device__ __forceinline__ void lds_words(const uint32_t* p, uint32_t (&w)[N]) {
+  if constexpr (N % 4 == 0 && STR % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      const uint4 x = *reinterpret_cast<const uint4*>(p + i);
+      w[i] = x.x; w[i + 1] = x.y; w[i + 2] = x.z; w[i + 3] = x.w;
+    }
+  } else if constexpr (N % 2 == 0 && STR % 2 == 0) {
+#pragma unroll
+    for (int i = 0; i < N; i += 2) {
+      const uint2 x = *reinterpret_cast<const uint2*>(p + i);
+      w[i] = x.x; w[i + 1] = x.y;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) w[i] = p[i];
+  }
+}
+
+// o[h][d] += sum_t p[t][h] * V[t][d] for the lane's DPL dims of HPV heads,
+// reading the tile's V rows (token-major, ROWB bytes each) from LDS.
 template <typename T, int HD, int REP>
-__device__ __forceinline__ void tile_pv(WaveState<T, HD, REP>& st,
-                                        const uint4 (&vr)[Geo<T, HD, REP>::RV], int vg,
-                                        bool rescale, const float* pbuf, const float* cbuf) {
+__device__ __forceinline__ void tile_pv(WaveState<T, HD, REP>& st, const unsigned char* vt,
+                                        int hg, int dl, bool rescale, const uint32_t* pbuf,
+                                        const float* cbuf) {
   using G = Geo<T, HD, REP>;
   if (rescale) {
-    float cr[G::REPP];
 #pragma unroll
-    for (int h = 0; h < REP; ++h) cr[h] = cbuf[h];
+    for (int i = 0; i < G::HPV; ++i) {
+      const float cr = cbuf[hg * G::HPV + i];
 #pragma unroll
-    for (int h = 0; h < REP; ++h)
-#pragma unroll
-      for (int e = 0; e < G::EPC; ++e) st.o[h][e] *= cr[h];
+      for (int e = 0; e < G::DPL; ++e) st.o[i][e] *= cr;
+    }
   }
-  if constexpr (sizeof(T) == 2) {
-    // bf16: two tokens at a time. Their probabilities are rounded to a bf16
-    // pair and their V values for one dimension are packed side by side, so
-    // one fp32-accumulating bf16 dot2 adds both tokens' terms.
-    static_assert(G::RV % 2 == 0, "bf16 V rows come in pairs");
+  const unsigned char* vl = vt + dl * G::DPL * G::ISZ;
+  if constexpr (G::ISZ == 2) {
+    // bf16: two tokens at a time. Their probabilities are a packed bf16 pair
+    // and their V values of one dimension are packed side by side, so one
+    // fp32-accumulating bf16 dot2 adds both tokens' terms.
+    constexpr int W = G::DPL / 2;   // words of V per token and lane
 #pragma unroll
-    for (int r = 0; r < G::RV; r += 2) {
-      const float* pa = pbuf + (r * G::TPW_V + vg) * G::REPP;
-      const float* pb = pbuf + ((r + 1) * G::TPW_V + vg) * G::REPP;
-      uint32_t pp[G::REPP];
+    for (int pp = 0; pp < G::TILE / 2; ++pp) {
+      uint32_t a[W], b[W], pr[G::HPV];
+      lds_words<W, G::ROWB / 4>(reinterpret_cast<const uint32_t*>(vl + 2 * pp * G::ROWB), a);
+      lds_words<W, G::ROWB / 4>(reinterpret_cast<const uint32_t*>(vl + (2 * pp + 1) * G::ROWB), b);
+      lds_words<G::HPV, G::PSTR>(pbuf + pp * G::PSTR + hg * G::HPV, pr);
 #pragma unroll
-      for (int h = 0; h < REP; ++h) pp[h] = pack_bf16x2(pa[h], pb[h]);
-      const uint32_t va[4] = {vr[r].x, vr[r].y, vr[r].z, vr[r].w};
-      const uint32_t vb[4] = {vr[r + 1].x, vr[r + 1].y, vr[r + 1].z, vr[r + 1].w};
+      for (int q = 0; q < W; ++q) {
+        const uint32_t lo = __builtin_amdgcn_perm(b[q], a[q], 0x05040100u);  // dim 2q
+        const uint32_t hi = __builtin_amdgcn_perm(b[q], a[q], 0x07060302u);  // dim 2q+1
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t lo = __builtin_amdgcn_perm(vb[q], va[q], 0x05040100u);  // dim 2q of a, b
-        const uint32_t hi = __builtin_amdgcn_perm(vb[q], va[q], 0x07060302u);  // dim 2q+1
-#pragma unroll
-        for (int h = 0; h < REP; ++h) {
-          st.o[h][2 * q] = dot2_bf16(pp[h], lo, st.o[h][2 * q]);
-          st.o[h][2 * q + 1] = dot2_bf16(pp[h], hi, st.o[h][2 * q + 1]);
+        for (int i = 0; i < G::HPV; ++i) {
+          st.o[i][2 * q] = dot2_bf16(pr[i], lo, st.o[i][2 * q]);
+          st.o[i][2 * q + 1] = dot2_bf16(pr[i], hi, st.o[i][2 * q + 1]);
         }
       }
     }
   } else {
+    const float* pf = reinterpret_cast<const float*>(pbuf);
 #pragma unroll
-    for (int r = 0; r < G::RV; ++r) {
-      const float* pp = pbuf + (r * G::TPW_V + vg) * G::REPP;
-      float pr[G::REPP];
+    for (int t = 0; t < G::TILE; ++t) {
+      uint32_t v[G::DPL], pr[G::HPV];
+      lds_words<G::DPL, G::ROWB / 4>(reinterpret_cast<const uint32_t*>(vl + t * G::ROWB), v);
+      lds_words<G::HPV, G::PSTR>(reinterpret_cast<const uint32_t*>(pf) + t * G::PSTR + hg * G::HPV,
+                                 pr);
 #pragma unroll
-      for (int h = 0; h < REP; ++h) pr[h] = pp[h];
-      float v[G::EPC];
-      chunk_to_f32<T>(vr[r], v);
+      for (int i = 0; i < G::HPV; ++i)
 #pragma unroll
-      for (int h = 0; h < REP; ++h)
-#pragma unroll
-        for (int e = 0; e < G::EPC; ++e) st.o[h][e] = fmaf(pr[h], v[e], st.o[h][e]);
+        for (int e = 0; e < G::DPL; ++e)
+          st.o[i][e] = fmaf(__uint_as_float(pr[i]), __uint_as_float(v[e]), st.o[i][e]);
     }
   }
 }
 
-constexpr int kStages = 2;   // tiles in a wave's LDS ring
-
-template <typename T, int HD, int REP>
-struct Ring {
-  using G = Geo<T, HD, REP>;
-  static constexpr int LOADS = G::RK * G::KCH + G::RV;   // 16-byte loads per lane per tile
-  static constexpr int STAGE = LOADS * 1024;              // bytes of one tile of one wave
+// Lane layout and addressing of one wave's part of a split.
+struct Lanes {
+  int lane, kg, kc, vg, hb, hg, dl;
+  bool dup0;
 };
 
-// The wave's full tiles from tb (step kStep) up to t_end. Tiles stream into the
-// wave's LDS ring kStages - 1 tiles ahead of the one being computed; each lane
-// reads back exactly the 16-byte pieces it loaded (conflict-free).
-template <typename T, int HD, int REP, bool UNI, int kStep>
-__device__ __forceinline__ void full_tiles(const SplitCtx& c, WaveState<T, HD, REP>& st,
-                                           const uint4 (&qr)[REP][Geo<T, HD, REP>::KCH], int tb,
-                                           int t_end, int lane, int kg, int kc, int vg, int hb,
-                                           bool dup0, float* pbuf, float* cbuf,
-                                           const unsigned char* ring) {
+// Issue the 16-byte direct-to-LDS loads of one tile (K rows, then V rows) into
+// LDS stage `base`. Unmasked uniform tiles address each row group from one
+// scalar block id; other tiles compute a per-lane address and read dead
+// tokens (past the split, or in an invalid block) from the zero row.
+template <typename T, int HD, int REP, bool UNI>
+__device__ __forceinline__ void issue_tile(const SplitCtx& c, const Lanes& ln, int tb,
+                                           const TileIds<Geo<T, HD, REP>::NID>& ti,
+                                           uint32_t base) {
   using G = Geo<T, HD, REP>;
-  using R = Ring<T, HD, REP>;
-  const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
   const int bmask = (1 << c.bshift) - 1;
-  auto issue = [&](int t, int stg) {
-    const uint32_t base = ring_lds + stg * R::STAGE;
+  if (UNI && !ti.masked) {
 #pragma unroll
     for (int r = 0; r < G::RK; ++r) {
-      const int tr = t + r * G::TPW_K;
-      if (UNI) {
-        const char* rb = row_base(c, c.kh, tr);
+      const int tr = tb + r * G::TPW_K;
+      const int blk = __builtin_amdgcn_readfirstlane(pick(ti, (r * G::TPW_K) >> c.bshift));
+      const char* rb = c.kh + (uint64_t)(uint32_t)blk * c.blk_bytes + (uint32_t)(tr & bmask) * c.rsb;
 #pragma unroll
-        for (int i = 0; i < G::KCH; ++i)
-          dma16s(rb + i * G::LPT_K * 16, c.koff, base + (r * G::KCH + i) * 1024);
-      } else {
-        const int tt = tr + kg;
-        const int blk = c.tbl[(tt >> c.bshift) - c.tbl_base];
-        const char* p = c.kb + (uint64_t)(uint32_t)blk * c.blk_bytes + (uint32_t)(tt & bmask) * c.rsb;
-#pragma unroll
-        for (int i = 0; i < G::KCH; ++i)
-          dma16(p + i * G::LPT_K * 16, base + (r * G::KCH + i) * 1024);
-      }
+      for (int i = 0; i < G::KCH; ++i)
+        dma16s(rb + i * G::LPT_K * 16, c.koff, base + (r * G::KCH + i) * 1024);
     }
 #pragma unroll
     for (int r = 0; r < G::RV; ++r) {
-      const int tr = t + r * G::TPW_V;
-      const uint32_t dst = base + (G::RK * G::KCH + r) * 1024;
-      if (UNI) {
-        dma16s(row_base(c, c.vh, tr), c.voff, dst);
-      } else {
-        const int tt = tr + vg;
-        const int blk = c.tbl[(tt >> c.bshift) - c.tbl_base];
-        dma16(c.vb + (uint64_t)(uint32_t)blk * c.blk_bytes + (uint32_t)(tt & bmask) * c.rsb, dst);
-      }
+      const int tr = tb + r * G::TPW_V;
+      const int blk = __builtin_amdgcn_readfirstlane(pick(ti, (r * G::TPW_V) >> c.bshift));
+      const char* rb = c.vh + (uint64_t)(uint32_t)blk * c.blk_bytes + (uint32_t)(tr & bmask) * c.rsb;
+      dma16s(rb, c.voff, base + (G::RK * G::KCH + r) * 1024);
     }
-  };
-  const int n = (t_end - 1 - tb) / kStep + 1;   // tiles of this wave
-  // The prologue's own loads (q) are back before the ring starts. Issued as the
-  // builtin so the compiler's wait bookkeeping sees it (and inserts no waits for
-  // q inside the loop, where they would also stall on the ring's loads).
-  __builtin_amdgcn_s_waitcnt(0);
-#pragma unroll
-  for (int q = 0; q < kStages - 1; ++q)
-    if (q < n) issue(tb + q * kStep, q);
-  for (int k = 0; k < n; ++k) {
-    if (k + kStages - 1 < n) {
-      wait_lgkmcnt0();   // the stage about to be refilled has been read
-      issue(tb + (k + kStages - 1) * kStep, (k + kStages - 1) % kStages);
-      wait_vmcnt<(kStages - 1) * R::LOADS>();
+    return;
+  }
+  auto row = [&](int tt, const char* lb, const char* zb) -> const char* {
+    int blk;
+    bool ok = tt < c.t1;
+    if (UNI) {
+      const int i = (tt - tb) >> c.bshift;
+      blk = pick(ti, i);
+      ok = ok && ((ti.ok >> i) & 1u);
     } else {
-      wait_vmcnt<0>();
+      blk = ok ? c.tbl[(tt >> c.bshift) - c.tbl_base] : -1;
+      ok = blk >= 0;
     }
-    const uint4* sp = reinterpret_cast<const uint4*>(ring + (k % kStages) * R::STAGE) + lane;
-    uint4 kr[G::RK][G::KCH];
-    uint4 vr[G::RV];
-    bool kval[G::RK];
+    return ok ? lb + (uint64_t)(uint32_t)blk * c.blk_bytes + (uint32_t)(tt & bmask) * c.rsb : zb;
+  };
 #pragma unroll
-    for (int r = 0; r < G::RK; ++r)
+  for (int r = 0; r < G::RK; ++r) {
+    const char* p = row(tb + r * G::TPW_K + ln.kg, c.kb, c.kz);
 #pragma unroll
-      for (int i = 0; i < G::KCH; ++i) kr[r][i] = sp[(r * G::KCH + i) * 64];
+    for (int i = 0; i < G::KCH; ++i) dma16(p + i * G::LPT_K * 16, base + (r * G::KCH + i) * 1024);
+  }
 #pragma unroll
-    for (int r = 0; r < G::RV; ++r) vr[r] = sp[(G::RK * G::KCH + r) * 64];
-    float sc[G::RK][G::HPL];
-    tile_scores<T, HD, REP, false>(c, kc, qr, kr, kval, sc);
-    const bool moved = tile_softmax<T, HD, REP>(st, sc, kg, hb, dup0, pbuf, cbuf);
-    tile_pv<T, HD, REP>(st, vr, vg, moved, pbuf, cbuf);
+  for (int r = 0; r < G::RV; ++r)
+    dma16(row(tb + r * G::TPW_V + ln.vg, c.vb, c.vz), base + (G::RK * G::KCH + r) * 1024);
+}
+
+template <typename T, int HD, int REP, bool UNI>
+__device__ __forceinline__ void compute_tile(const SplitCtx& c, const Lanes& ln,
+                                             WaveState<T, HD, REP>& st,
+                                             const uint4 (&qr)[REP][Geo<T, HD, REP>::KCH], int tb,
+                                             const TileIds<Geo<T, HD, REP>::NID>& ti,
+                                             const unsigned char* stage, uint32_t* pbuf,
+                                             float* cbuf) {
+  using G = Geo<T, HD, REP>;
+  const uint4* sp = reinterpret_cast<const uint4*>(stage) + ln.lane;
+  uint4 kr[G::RK][G::KCH];
+#pragma unroll
+  for (int r = 0; r < G::RK; ++r)
+#pragma unroll
+    for (int i = 0; i < G::KCH; ++i) kr[r][i] = sp[(r * G::KCH + i) * 64];
+  float sc[G::RK][G::HPL];
+  bool kval[G::RK];
+#pragma unroll
+  for (int r = 0; r < G::RK; ++r) kval[r] = true;
+  if (ti.masked) {
+#pragma unroll
+    for (int r = 0; r < G::RK; ++r) kval[r] = live<T, HD, REP, UNI>(c, ti, tb, tb + r * G::TPW_K + ln.kg);
+    tile_scores<T, HD, REP, true>(c, ln.kc, qr, kr, kval, sc);
+  } else {
+    tile_scores<T, HD, REP, false>(c, ln.kc, qr, kr, kval, sc);
+  }
+  const bool moved = tile_softmax<T, HD, REP>(st, sc, ln.kg, ln.hb, ln.dup0, pbuf, cbuf);
+  tile_pv<T, HD, REP>(st, stage + G::VOFF, ln.hg, ln.dl, moved, pbuf, cbuf);
+}
+
+template <int LOADS, int S>
+__device__ __forceinline__ void wait_tiles_after(int behind) {
+  // loads of `behind` newer tiles may stay in flight (behind < S)
+  if constexpr (S > 3) {
+    if (behind >= 3) { wait_vmcnt<3 * LOADS>(); return; }
+  }
+  if constexpr (S > 2) {
+    if (behind == 2) { wait_vmcnt<2 * LOADS>(); return; }
+  }
+  if (behind == 1) { wait_vmcnt<LOADS>(); return; }
+  wait_vmcnt<0>();
+}
+
+// The wave's tiles tb0, tb0 + kStep, ... below t1. Tiles stream into the wave's
+// STAGES-deep LDS ring, STAGES - 1 tiles ahead of the one being computed.
+template <typename T, int HD, int REP, bool UNI, int kStep>
+__device__ __forceinline__ void wave_tiles(const SplitCtx& c, const Lanes& ln,
+                                           WaveState<T, HD, REP>& st,
+                                           const uint4 (&qr)[REP][Geo<T, HD, REP>::KCH], int tb0,
+                                           bool any_bad, uint32_t* pbuf, float* cbuf,
+                                           int* idslots, const unsigned char* ring) {
+  using G = Geo<T, HD, REP>;
+  using TI = TileIds<G::NID>;
+  constexpr int S = G::STAGES;
+  constexpr int TPB = 64 / G::NID;
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
+  const uint32_t slots_lds = (uint32_t)(uintptr_t)idslots;
+  const int n = (c.t1 - 1 - tb0) / kStep + 1;   // tiles of this wave (tb0 < t1)
+  auto ids = [&](int m) -> TI {
+    const int tb = tb0 + m * kStep;
+    if (UNI) return read_ids<T, HD, REP>(c, tb, m, idslots);
+    TI ti;
+#pragma unroll
+    for (int i = 0; i < G::NID; ++i) ti.id[i] = 0;
+    ti.ok = 0;
+    ti.masked = any_bad || tb + G::TILE > c.t1;
+    return ti;
+  };
+  if (UNI) {
+    ids_batch_dma<T, HD, REP>(c, tb0, kStep, n, 0, ln.lane, slots_lds);
+    if (n > TPB) ids_batch_dma<T, HD, REP>(c, tb0, kStep, n, 1, ln.lane, slots_lds);
+  }
+  // The prologue's own loads (q, table) are back before the ring starts, so the
+  // compiler puts no waits for them inside the loop (where they would also
+  // stall on the ring's loads).
+  __builtin_amdgcn_s_waitcnt(0);
+  TI ti[S];
+#pragma unroll
+  for (int q = 0; q < S - 1; ++q) {
+    ti[q] = ti[0];
+    if (q < n) {
+      ti[q] = ids(q);
+      issue_tile<T, HD, REP, UNI>(c, ln, tb0 + q * kStep, ti[q], ring_lds + q * G::STAGE);
+    }
+  }
+  for (int k = 0; k < n; ++k) {
+    const int m = k + S - 1;   // tile issued in this iteration
+    if (m < n) {
+      wait_lgkmcnt0();   // the stage about to be refilled has been read
+      ti[S - 1] = ids(m);
+      if (UNI && m % TPB == 0 && m > 0 && (m / TPB + 1) * TPB < n)
+        ids_batch_dma<T, HD, REP>(c, tb0, kStep, n, m / TPB + 1, ln.lane, slots_lds);
+      issue_tile<T, HD, REP, UNI>(c, ln, tb0 + m * kStep, ti[S - 1],
+                                  ring_lds + (m % S) * G::STAGE);
+      wait_vmcnt<(S - 1) * G::LOADS>();
+    } else {
+      wait_tiles_after<G::LOADS, S>(n - 1 - k);
+    }
+    compute_tile<T, HD, REP, UNI>(c, ln, st, qr, tb0 + k * kStep, ti[0], ring + (k % S) * G::STAGE,
+                                  pbuf, cbuf);
+#pragma unroll
+    for (int q = 0; q < S - 1; ++q) ti[q] = ti[q + 1];
   }
 }
 
 __host__ __device__ constexpr int round16(int b) { return (b + 15) & ~15; }
 
-// Query heads of a group are split over HS waves when the group is large:
-// each wave then holds q and o for REP/HS heads only (fewer registers, more
-// resident waves); the HS waves of a pair read the same K/V rows.
-template <int REP>
-struct HeadSplit {
-  static constexpr int HS = 1;
-  static constexpr int REPW = REP / HS;              // query heads per wave
-  static constexpr int NSTREAM = kWaves / HS;       // token streams per workgroup
-};
-
 template <typename T, int HD, int REP>
 struct Lds {
-  using H = HeadSplit<REP>;
-  using G = Geo<T, HD, H::REPW>;
-  static constexpr int kWaveFloats = G::TILE * G::REPP + G::REPP;   // probabilities + rescale
-  static constexpr int kMergeFloats = H::REPW * (HD + 2);           // m, l, o per wave
-  static constexpr int kRingBytes = kStages * Ring<T, HD, H::REPW>::STAGE;  // per wave
+  using G = Geo<T, HD, REP>;
+  // per wave: two 64-entry block id slots, probabilities, rescale factors
+  static constexpr int kWaveWords = 128 + round16((G::PROWS * G::PSTR + G::PSTR) * 4) / 4;
+  static constexpr int kMergeFloats = REP * (HD + 2);                                 // m, l, o per wave
+  static constexpr int kRingBytes = G::STAGES * G::STAGE;                             // per wave
   __host__ __device__ static int ring_offset(int tbl_entries) {
-    return round16(tbl_entries * 4) + kWaves * kWaveFloats * 4;
+    return round16(tbl_entries * 4) + kWaves * kWaveWords * 4;
   }
   // The merge area reuses the front of LDS once every wave has left the tile loop.
-  static int bytes(int tbl_entries) {
+  __host__ __device__ static int bytes(int tbl_entries) {
     const int loop = ring_offset(tbl_entries) + kWaves * kRingBytes;
     const int merge = kWaves * kMergeFloats * 4;
     return loop > merge ? loop : merge;
   }
+  // Table entries staged in LDS: only the per-lane path uses them.
+  __host__ __device__ static int table_entries(int partition, int bshift) {
+    return uniform(bshift) ? 0 : (partition >> bshift) + 1;
+  }
+  __host__ __device__ static bool uniform(int bshift) {
+    return G::TPW_K <= (1 << bshift) && G::TPW_V <= (1 << bshift);
+  }
 };
+
+// 16-byte pieces of dead tokens are read from here (longest row: fp32 x 256).
+__device__ __attribute__((aligned(16))) unsigned char g_zero_row[1024];
 
 template <typename T, int HD, int REP>
 __global__ void __launch_bounds__(kThreads)
 decode_partials_kernel(DecodeArgs a) {
-  using H = HeadSplit<REP>;
-  constexpr int REPW = H::REPW;
-  using G = Geo<T, HD, REPW>;
+  using G = Geo<T, HD, REP>;
   using L = Lds<T, HD, REP>;
   extern __shared__ __align__(16) unsigned char smem[];
 
+  // Splits are dispatched last-index first: the later splits exist only for
+  // the longer sequences, so their work starts early and the tail of the
+  // launch is made of the short first splits.
   const int g = blockIdx.x;
-  int j = blockIdx.y, s = blockIdx.z;
+  int s = blockIdx.y, j = gridDim.z - 1 - blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
-  const int hh = w % H::HS, stream = w / H::HS;             // head half, token stream
   const int bshift = a.block_shift;
   const int lim = min(a.max_ctx, a.max_blocks << bshift);
   int qrow = s;   // row of q and out
@@ -598,142 +709,133 @@ decode_partials_kernel(DecodeArgs a) {
   }
   const int t0 = j * P;
   const int t1 = min(ctx, t0 + P);
+  const bool uni = L::uniform(bshift);
 
-  const int tbl_entries = (P >> bshift) + 1;
+  const int tbl_entries = L::table_entries(P, bshift);
   int* tbl = reinterpret_cast<int*>(smem);
-  float* pbuf = reinterpret_cast<float*>(smem + round16(tbl_entries * 4)) + w * L::kWaveFloats;
-  float* cbuf = pbuf + G::TILE * G::REPP;
+  int* idslot = reinterpret_cast<int*>(smem + round16(tbl_entries * 4)) + w * L::kWaveWords;
+  uint32_t* pbuf = reinterpret_cast<uint32_t*>(idslot + 128);
+  float* cbuf = reinterpret_cast<float*>(pbuf + G::PROWS * G::PSTR);
   float* merge = reinterpret_cast<float*>(smem);
   const unsigned char* ring = smem + L::ring_offset(tbl_entries) + w * L::kRingBytes;
 
-  // ---- stage this split's block ids in LDS (invalid ids become -1)
-  const int tbl_base = t0 >> bshift;
-  const int nb = ((t1 - 1) >> bshift) - tbl_base + 1;
-  const int* trow = a.tables + (size_t)s * a.max_blocks + tbl_base;
-  int bad = 0;
-  for (int i = tid; i < nb; i += kThreads) {
-    const int id = trow[i];
-    const bool ok = (unsigned)id < (unsigned)a.num_blocks;
-    tbl[i] = ok ? id : -1;
-    bad |= !ok;
+  SplitCtx c;
+  c.trow = a.tables + (size_t)s * a.max_blocks;
+  c.tbl = tbl;
+  c.tbl_base = t0 >> bshift;
+  c.bshift = bshift;
+  c.num_blocks = a.num_blocks;
+  c.t1 = t1;
+  c.scale_log2 = a.scale_log2;
+
+  // ---- per-lane path: stage this split's block ids in LDS (invalid -> -1)
+  int any_bad = 0;
+  if (!uni) {
+    const int nb = ((t1 - 1) >> bshift) - c.tbl_base + 1;
+    int bad = 0;
+    for (int i = tid; i < nb; i += kThreads) {
+      const int id = c.trow[c.tbl_base + i];
+      const bool ok = (unsigned)id < (unsigned)a.num_blocks;
+      tbl[i] = ok ? id : -1;
+      bad |= !ok;
+    }
+    any_bad = __syncthreads_or(bad);
   }
-  const int any_bad = __syncthreads_or(bad);
 
   // ---- this wave's query heads, in the K-stage lane layout
-  const int kg = lane / G::LPT_K, kc = lane % G::LPT_K;
-  const int vg = lane / G::LPT_V, vc = lane % G::LPT_V;
-  const T* qp = reinterpret_cast<const T*>(a.q) +
-                ((size_t)qrow * a.num_q_heads + hq0 + hh * REPW) * HD;
-  uint4 qr[REPW][G::KCH];
+  Lanes ln;
+  ln.lane = lane;
+  ln.kg = lane / G::LPT_K;
+  ln.kc = lane % G::LPT_K;
+  ln.vg = lane / G::LPT_V;
+  const int vc = lane % G::LPT_V;
+  ln.hg = lane / G::LPH;
+  ln.dl = lane % G::LPH;
+  ln.hb = head_base<G::LPT_K, G::REPP, G::HPL>(ln.kc);
+  ln.dup0 = (ln.kc & (G::DUP - 1)) == 0;
+  const T* qp = reinterpret_cast<const T*>(a.q) + ((size_t)qrow * a.num_q_heads + hq0) * HD;
+  uint4 qr[REP][G::KCH];
 #pragma unroll
-  for (int h = 0; h < REPW; ++h)
+  for (int h = 0; h < REP; ++h)
 #pragma unroll
     for (int i = 0; i < G::KCH; ++i)
-      qr[h][i] = *reinterpret_cast<const uint4*>(qp + h * HD + (kc + i * G::LPT_K) * G::EPC);
+      qr[h][i] = *reinterpret_cast<const uint4*>(qp + h * HD + (ln.kc + i * G::LPT_K) * G::EPC);
 
-  SplitCtx c;
   {
     const size_t head_off = (size_t)g * HD * G::ISZ;
     c.kh = reinterpret_cast<const char*>(a.k_pool) + head_off;
     c.vh = reinterpret_cast<const char*>(a.v_pool) + head_off;
-    c.kb = c.kh + kc * 16;
+    c.kb = c.kh + ln.kc * 16;
     c.vb = c.vh + vc * 16;
-    c.tbl = tbl;
-    c.tbl_base = tbl_base;
-    c.bshift = bshift;
+    c.kz = reinterpret_cast<const char*>(g_zero_row) + ln.kc * 16;
+    c.vz = reinterpret_cast<const char*>(g_zero_row) + vc * 16;
     c.rsb = (uint32_t)a.num_kv_heads * HD * G::ISZ;
     c.blk_bytes = c.rsb << bshift;
-    c.koff = (uint32_t)kg * c.rsb + kc * 16;
-    c.voff = (uint32_t)vg * c.rsb + vc * 16;
-    c.t1 = t1;
-    c.scale_log2 = a.scale_log2;
+    c.koff = (uint32_t)ln.kg * c.rsb + ln.kc * 16;
+    c.voff = (uint32_t)ln.vg * c.rsb + vc * 16;
   }
-  const int hb = head_base<G::LPT_K, G::REPP, G::HPL>(kc);
-  const bool dup0 = (kc & (G::DUP - 1)) == 0;
 
-  WaveState<T, HD, REPW> st;
+  WaveState<T, HD, REP> st;
 #pragma unroll
   for (int jj = 0; jj < G::HPL; ++jj) {
     st.m[jj] = -INFINITY;
     st.lsum[jj] = 0.f;
   }
 #pragma unroll
-  for (int h = 0; h < REPW; ++h)
+  for (int i = 0; i < G::HPV; ++i)
 #pragma unroll
-    for (int e = 0; e < G::EPC; ++e) st.o[h][e] = 0.f;
+    for (int e = 0; e < G::DPL; ++e) st.o[i][e] = 0.f;
 
-  // ---- full tiles: pipelined; the partial last tile (or all, with a bad id): masked
-  const int n_full = any_bad ? 0 : (t1 - t0) / G::TILE;
-  const int n_tiles = (t1 - t0 + G::TILE - 1) / G::TILE;
-  constexpr int kStep = H::NSTREAM * G::TILE;
-  const int t_full_end = t0 + n_full * G::TILE;
-  int tb = t0 + stream * G::TILE;
-  if (tb < t_full_end) {
-    const bool uni = G::TPW_K <= (1 << bshift) && G::TPW_V <= (1 << bshift);
+  // ---- tiles w, w + 4, ... of the split, every one through the LDS ring
+  constexpr int kStep = kWaves * G::TILE;
+  const int tb0 = t0 + w * G::TILE;
+  if (tb0 < t1) {
     if (uni)
-      full_tiles<T, HD, REPW, true, kStep>(c, st, qr, tb, t_full_end, lane, kg, kc, vg, hb,
-                                          dup0, pbuf, cbuf, ring);
+      wave_tiles<T, HD, REP, true, kStep>(c, ln, st, qr, tb0, false, pbuf, cbuf, idslot, ring);
     else
-      full_tiles<T, HD, REPW, false, kStep>(c, st, qr, tb, t_full_end, lane, kg, kc, vg, hb,
-                                           dup0, pbuf, cbuf, ring);
-    tb += ((t_full_end - 1 - tb) / kStep + 1) * kStep;
-  }
-  for (int k = (tb - t0) / G::TILE; k < n_tiles; k += H::NSTREAM) {
-    const int tm = t0 + k * G::TILE;
-    uint4 kr[G::RK][G::KCH];
-    uint4 vr[G::RV];
-    bool kval[G::RK];
-    load_k<T, HD, REPW, true>(c, tm, kg, kr, kval);
-    load_v<T, HD, REPW, true>(c, tm, vg, vr);
-    float sc[G::RK][G::HPL];
-    tile_scores<T, HD, REPW, true>(c, kc, qr, kr, kval, sc);
-    const bool moved = tile_softmax<T, HD, REPW>(st, sc, kg, hb, dup0, pbuf, cbuf);
-    tile_pv<T, HD, REPW>(st, vr, vg, moved, pbuf, cbuf);
+      wave_tiles<T, HD, REP, false, kStep>(c, ln, st, qr, tb0, any_bad, pbuf, cbuf, idslot,
+                                            ring);
   }
 
   // ---- per-wave totals, then merge the waves in LDS
   float* mw = merge + w * L::kMergeFloats;
 #pragma unroll
   for (int jj = 0; jj < G::HPL; ++jj) st.lsum[jj] = strided_reduce<G::LPT_K, false>(st.lsum[jj]);
-#pragma unroll
-  for (int h = 0; h < REPW; ++h)
-#pragma unroll
-    for (int e = 0; e < G::EPC; ++e) st.o[h][e] = strided_sum<G::LPT_V>(st.o[h][e]);
   __syncthreads();  // every wave is done with the table and tile buffers
-  if (kg == 0 && dup0) {
+  if (ln.kg == 0 && ln.dup0) {
 #pragma unroll
     for (int jj = 0; jj < G::HPL; ++jj) {
-      const int h = hb + jj;
-      if (h < REPW) {
+      const int h = ln.hb + jj;
+      if (h < REP) {
         mw[h] = st.m[jj];
-        mw[REPW + h] = st.lsum[jj];
+        mw[REP + h] = st.lsum[jj];
       }
     }
   }
-  if (vg == 0) {
 #pragma unroll
-    for (int h = 0; h < REPW; ++h)
+  for (int i = 0; i < G::HPV; ++i) {
+    const int h = ln.hg * G::HPV + i;
+    if (h < REP) {
 #pragma unroll
-      for (int e = 0; e < G::EPC; ++e) mw[2 * REPW + h * HD + vc * G::EPC + e] = st.o[h][e];
+      for (int e = 0; e < G::DPL; ++e) mw[2 * REP + h * HD + ln.dl * G::DPL + e] = st.o[i][e];
+    }
   }
   __syncthreads();
 
   const int J = a.num_splits;
   for (int idx = tid; idx < REP * HD; idx += kThreads) {
     const int h = idx / HD, d = idx % HD;
-    const int hw = h / REPW, hl = h % REPW;   // head half and head within it
     float M = -INFINITY;
 #pragma unroll
-    for (int ss = 0; ss < H::NSTREAM; ++ss)
-      M = fmaxf(M, merge[(ss * H::HS + hw) * L::kMergeFloats + hl]);
+    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, merge[ww * L::kMergeFloats + h]);
     float Ls = 0.f, O = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int ss = 0; ss < H::NSTREAM; ++ss) {
-        const float* mv = merge + (ss * H::HS + hw) * L::kMergeFloats;
-        const float f = fast_exp2(mv[hl] - M);
-        Ls = fmaf(mv[REPW + hl], f, Ls);
-        O = fmaf(mv[2 * REPW + hl * HD + d], f, O);
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const float* mv = merge + ww * L::kMergeFloats;
+        const float f = fast_exp2(mv[h] - M);
+        Ls = fmaf(mv[REP + h], f, Ls);
+        O = fmaf(mv[2 * REP + h * HD + d], f, O);
       }
     }
     if (nsplit == 1) {
@@ -784,11 +886,12 @@ __global__ void __launch_bounds__(64) decode_reduce_kernel(DecodeArgs a, int hea
   }
 }
 
+
 template <typename T, int HD, int REP>
 pkv_status launch_split(const DecodeArgs& a, hipStream_t st) {
-  const int tbl_entries = (a.partition >> a.block_shift) + 1;
-  const int lds = Lds<T, HD, REP>::bytes(tbl_entries);
-  dim3 grid(a.num_kv_heads, a.num_splits, a.num_seqs);
+  using L = Lds<T, HD, REP>;
+  const int lds = L::bytes(L::table_entries(a.partition, a.block_shift));
+  dim3 grid(a.num_kv_heads, a.num_seqs, a.num_splits);
   if (a.cu_q) {
     const int z = a.total_q < kRowGridZ ? a.total_q : kRowGridZ;
     grid = dim3(a.num_kv_heads, (a.total_q + z - 1) / z, z);
@@ -831,7 +934,7 @@ pkv_status dispatch_hd(const DecodeArgs& a, int hd, int rep, hipStream_t st) {
 }  // namespace
 
 int decode_tile_tokens(int row_bytes) {
-  return row_bytes >= 1024 ? 4 : row_bytes >= 512 ? 8 : row_bytes >= 256 ? 16 : row_bytes >= 128 ? 32 : 64;
+  return row_bytes >= 1024 ? 2 : row_bytes >= 512 ? 4 : row_bytes >= 256 ? 8 : row_bytes >= 128 ? 32 : 64;
 }
 
 bool decode_supported(int dtype, int head_dim, int rep) {

@@ -177,6 +177,11 @@ __device__ __forceinline__ void dma16s(const char* sbase, uint32_t voff, uint32_
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"(sbase), "s"(lds) : "memory");
 }
+// The same for one 4-byte word per lane (lane i -> M0 + 4*i).
+__device__ __forceinline__ void dma4(const void* gaddr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(gaddr), "s"(lds) : "memory");
+}
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
