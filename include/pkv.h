@@ -190,9 +190,11 @@ pkv_status pkv_decode_reduce(const void* q, int32_t num_seqs, int32_t num_q_head
  * sequence's positions 0..a through its block table (its own K/V must already
  * be in the pool: write, then attend). Rows with a < 0 are zero.
  * cu_q: device int32 [num_seqs+1], non-decreasing from 0, cu_q[num_seqs] ==
- * total_q_rows; max_q_len >= every n_s. bf16 pools use bf16 matrix cores
- * (fp32 accumulation, probabilities rounded to bf16 for the PV product);
- * fp32 pools use fp32 vector arithmetic throughout.
+ * total_q_rows; max_q_len >= every n_s. bf16 pools with head_dim 64 or 128
+ * and at most 2048 table entries per sequence in reach (min(max_context_len,
+ * max_blocks_per_seq * block_size) / block_size) use bf16 matrix cores (fp32
+ * accumulation, probabilities rounded to bf16 for the PV product); other
+ * cases run each row as a one-split decode (fp32 pools in fp32 throughout).
  * ------------------------------------------------------------------------- */
 pkv_status pkv_prefill(const void* q, const int32_t* cu_q, int32_t num_seqs,
                        int32_t num_q_heads, int32_t max_q_len, int32_t total_q_rows,
