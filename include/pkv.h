@@ -182,6 +182,44 @@ pkv_status pkv_decode_reduce(const void* q, int32_t num_seqs, int32_t num_q_head
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * pkv_decode_step -- one decode step with the KV write fused in ([MV] section
+ * 4, decode_step: the new token's K/V is written into its slot, then the
+ * sequence attends over all its positions; [D16] "What I learned" item 2).
+ *
+ * k_new, v_new: device [num_seqs, num_kv_heads, head_dim], dtype of the pool:
+ * the new token of sequence s, at position context_lens[s] - 1 (the length
+ * counts the new token). Its rows are written into slot
+ * block_tables[s][p / block_size] * block_size + p % block_size of k_pool /
+ * v_pool (skipped when that table entry is outside [0, num_blocks), as
+ * pkv_write skips an out-of-range slot), and the attention reads position p
+ * from k_new / v_new directly. The result and the pool contents are
+ * bit-identical to pkv_slot_mapping + pkv_write + pkv_decode with the same
+ * partition; the two launches of the separate write are saved. A sequence of
+ * length 0 writes nothing and gets zeros. Slots written must be distinct
+ * across sequences (as for pkv_write). Other arguments, the workspace and the
+ * errors are those of pkv_decode; k_new and v_new must be 16-byte aligned.
+ *
+ * pkv_decode_step_partials is its first phase (the fused write and the split
+ * partials); pkv_decode_reduce with the same arguments completes it.
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_decode_step(const void* q, const void* k_new, const void* v_new,
+                           int32_t num_seqs, int32_t num_q_heads, void* k_pool,
+                           void* v_pool, const pkv_pool_desc* pool,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t max_context_len,
+                           float scale, int32_t partition, void* out, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+pkv_status pkv_decode_step_partials(const void* q, const void* k_new, const void* v_new,
+                                    int32_t num_seqs, int32_t num_q_heads, void* k_pool,
+                                    void* v_pool, const pkv_pool_desc* pool,
+                                    const int32_t* block_tables,
+                                    int32_t max_blocks_per_seq,
+                                    const int32_t* context_lens, int32_t max_context_len,
+                                    float scale, int32_t partition, void* out,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * pkv_prefill -- causal attention of a chunk of query rows over the pool
  * ([MV] section 4: scores + full((T,T), -inf).triu(1), softmax, weighted V).
  *

@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     PoolDesc,
     abi_version,
     decode,
+    decode_step,
     decode_partition,
     decode_workspace_bytes,
     load,

@@ -27,8 +27,8 @@ _STATUS = {0: "PKV_OK", 1: "PKV_ERR_NULL", 2: "PKV_ERR_DTYPE", 3: "PKV_ERR_SHAPE
 # Every symbol include/pkv.h declares.
 EXPORTS = ("pkv_slot_mapping", "pkv_write", "pkv_decode_partition",
            "pkv_decode_workspace_bytes", "pkv_decode", "pkv_decode_partials",
-           "pkv_decode_reduce", "pkv_prefill", "pkv_status_string", "pkv_last_error",
-           "pkv_abi_version")
+           "pkv_decode_reduce", "pkv_decode_step", "pkv_decode_step_partials", "pkv_prefill",
+           "pkv_status_string", "pkv_last_error", "pkv_abi_version")
 
 
 class PkvError(RuntimeError):
@@ -72,6 +72,12 @@ def load(path: str | None = None):
     for name in ("pkv_decode", "pkv_decode_partials", "pkv_decode_reduce"):
         f = getattr(lib, name)
         f.argtypes = dec_args
+        f.restype = ctypes.c_int
+    step_args = [_P, _P, _P, _I, _I, _P, _P, ctypes.POINTER(PoolDesc), _P, _I, _P, _I,
+                 ctypes.c_float, _I, _P, _P, ctypes.c_size_t, _P]
+    for name in ("pkv_decode_step", "pkv_decode_step_partials"):
+        f = getattr(lib, name)
+        f.argtypes = step_args
         f.restype = ctypes.c_int
     lib.pkv_prefill.argtypes = [_P, _P, _I, _I, _I, _I, _P, _P, ctypes.POINTER(PoolDesc), _P,
                                 _I, _P, _I, ctypes.c_float, _P, _P]
@@ -213,6 +219,49 @@ def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                                _ptr(block_tables), maxb, _ptr(context_lens),
                                int(max_context_len), float(scale), int(partition), _ptr(out),
                                _ptr(workspace), ws_bytes, _stream()))
+    return out
+
+
+def decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                k_pool: torch.Tensor, v_pool: torch.Tensor, block_tables: torch.Tensor,
+                context_lens: torch.Tensor, scale: float, max_context_len: int,
+                out: torch.Tensor | None = None, partition: int = 0,
+                workspace: torch.Tensor | None = None, phase: str = "both") -> torch.Tensor:
+    """Decode step with the KV write fused in: k_new / v_new [S, Hkv, hd] are the
+    new token of each sequence (position context_lens - 1); they are written into
+    their slots and attended. ``phase``: "both", "partials" (then call
+    ``decode(..., phase="reduce")`` with the same arguments) or "reduce"."""
+    desc = _check_pools(k_pool, v_pool)
+    _dev(q, "q", k_pool.dtype)
+    _need(q.dim() == 3 and q.shape[2] == desc.head_dim, "q must be [S, Hq, head_dim]")
+    S, Hq, _ = q.shape
+    _dev(k_new, "k_new", k_pool.dtype, (S, desc.num_kv_heads, desc.head_dim))
+    _dev(v_new, "v_new", k_pool.dtype, (S, desc.num_kv_heads, desc.head_dim))
+    _dev(block_tables, "block_tables", torch.int32)
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == S,
+          "block_tables must be [S, max_blocks_per_seq]")
+    maxb = block_tables.shape[1]
+    _dev(context_lens, "context_lens", torch.int32, (S,))
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype, q.shape)
+    need = decode_workspace_bytes(S, Hq, max_context_len, k_pool, partition)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace", torch.uint8)
+        ws_bytes = workspace.numel()
+    lib = load()
+    common = (ctypes.byref(desc), _ptr(block_tables), maxb, _ptr(context_lens),
+              int(max_context_len), float(scale), int(partition), _ptr(out), _ptr(workspace),
+              ws_bytes, _stream())
+    if phase == "reduce":
+        _check(lib.pkv_decode_reduce(_ptr(q), S, Hq, _ptr(k_pool), _ptr(v_pool), *common))
+    else:
+        fn = lib.pkv_decode_step if phase == "both" else lib.pkv_decode_step_partials
+        _need(phase in ("both", "partials"), f"unknown phase {phase!r}")
+        _check(fn(_ptr(q), _ptr(k_new), _ptr(v_new), S, Hq, _ptr(k_pool), _ptr(v_pool), *common))
     return out
 
 

@@ -151,7 +151,7 @@ pkv_status decode_impl(Phase phase, const void* q, int32_t num_seqs, int32_t num
                        const int32_t* block_tables, int32_t max_blocks,
                        const int32_t* context_lens, int32_t max_ctx, float scale,
                        int32_t partition, void* out, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+                       void* stream, const void* k_new = nullptr, const void* v_new = nullptr) {
   DecodePlan plan;
   pkv_status st = plan_decode(num_seqs, num_q_heads, max_blocks, max_ctx, partition, pool,
                               &plan);
@@ -208,6 +208,8 @@ pkv_status decode_impl(Phase phase, const void* q, int32_t num_seqs, int32_t num
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.cu_q = nullptr;
   a.total_q = 0;
+  a.k_new = k_new;
+  a.v_new = v_new;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (phase != Phase::kReduce) {
     st = launch_decode_partials(a, pool->dtype, pool->head_dim, plan.rep, s);
@@ -372,6 +374,51 @@ pkv_status pkv_decode_reduce(const void* q, int32_t num_seqs, int32_t num_q_head
   return decode_impl(Phase::kReduce, q, num_seqs, num_q_heads, k_pool, v_pool, pool,
                      block_tables, max_blocks_per_seq, context_lens, max_context_len, scale,
                      partition, out, workspace, workspace_bytes, stream);
+}
+
+namespace {
+pkv_status check_step(const void* k_new, const void* v_new) {
+  if (!k_new || !v_new) {
+    set_error("k_new and v_new must not be NULL");
+    return PKV_ERR_NULL;
+  }
+  if (!aligned16(k_new) || !aligned16(v_new)) {
+    set_error("k_new and v_new must be 16-byte aligned");
+    return PKV_ERR_ALIGN;
+  }
+  return PKV_OK;
+}
+}  // namespace
+
+pkv_status pkv_decode_step(const void* q, const void* k_new, const void* v_new,
+                           int32_t num_seqs, int32_t num_q_heads, void* k_pool, void* v_pool,
+                           const pkv_pool_desc* pool, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t max_context_len, float scale, int32_t partition, void* out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0) {
+    const pkv_status st = check_step(k_new, v_new);
+    if (st != PKV_OK) return st;
+  }
+  return decode_impl(Phase::kBoth, q, num_seqs, num_q_heads, k_pool, v_pool, pool, block_tables,
+                     max_blocks_per_seq, context_lens, max_context_len, scale, partition, out,
+                     workspace, workspace_bytes, stream, k_new, v_new);
+}
+
+pkv_status pkv_decode_step_partials(const void* q, const void* k_new, const void* v_new,
+                                    int32_t num_seqs, int32_t num_q_heads, void* k_pool,
+                                    void* v_pool, const pkv_pool_desc* pool,
+                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t* context_lens, int32_t max_context_len,
+                                    float scale, int32_t partition, void* out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0) {
+    const pkv_status st = check_step(k_new, v_new);
+    if (st != PKV_OK) return st;
+  }
+  return decode_impl(Phase::kPartials, q, num_seqs, num_q_heads, k_pool, v_pool, pool,
+                     block_tables, max_blocks_per_seq, context_lens, max_context_len, scale,
+                     partition, out, workspace, workspace_bytes, stream, k_new, v_new);
 }
 
 pkv_status pkv_prefill(const void* q, const int32_t* cu_q, int32_t num_seqs, int32_t num_q_heads,

@@ -224,15 +224,13 @@ struct WaveState {
   float o[G::HPV][G::DPL];  // unnormalised output: DPL dims of HPV heads (PV layout)
 };
 
+// 16-byte pieces of dead tokens are read from here (longest row: fp32 x 256).
+__device__ __attribute__((aligned(16))) unsigned char g_zero_row[1024];
+
+// Wave-uniform description of one split (scalar registers).
 struct SplitCtx {
-  const char* kb;     // lane base into k_pool: + g*HD*isz + kc*16
-  const char* vb;     // lane base into v_pool: + g*HD*isz + vc*16
-  const char* kh;     // head base into k_pool: + g*HD*isz (uniform)
-  const char* vh;     // head base into v_pool: + g*HD*isz (uniform)
-  const char* kz;     // lane's K chunk in the zero row
-  const char* vz;     // lane's V chunk in the zero row
-  uint32_t koff;      // lane offset of its K chunk within a row group: kg*rsb + kc*16
-  uint32_t voff;      // lane offset of its V chunk within a row group: vg*rsb + vc*16
+  const char* kh;     // head base into k_pool: + g*HD*isz
+  const char* vh;     // head base into v_pool: + g*HD*isz
   const int* trow;    // this sequence's block table row (global)
   const int* tbl;     // LDS block ids of this split (-1 = invalid); per-lane path only
   int tbl_base;       // logical block index of tbl[0]
@@ -242,6 +240,9 @@ struct SplitCtx {
   uint32_t rsb;       // bytes of one token row (all heads)
   int t1;             // end of the split (exclusive)
   float scale_log2;
+  int tnew;           // position read from k_new/v_new (fused step), else -1
+  const char* knew;   // k_new row of this sequence and head (fused step)
+  const char* vnew;
 };
 
 // Block ids of one tile on the uniform path (every 16-byte load instruction of
@@ -296,7 +297,8 @@ __device__ __forceinline__ TileIds<Geo<T, HD, REP>::NID> read_ids(const SplitCtx
     ti.id[i] = ok ? id : 0;
     ti.ok |= (uint32_t)ok << i;
   }
-  ti.masked = tb + G::TILE > c.t1 || ti.ok != (2u << (lb - fb)) - 1u;
+  ti.masked = tb + G::TILE > c.t1 || ti.ok != (2u << (lb - fb)) - 1u ||
+              (c.tnew >= tb && c.tnew < tb + G::TILE);
   return ti;
 }
 
@@ -464,10 +466,12 @@ __device__ __forceinline__ void tile_pv(WaveState<T, HD, REP>& st, const unsigne
   }
 }
 
-// Lane layout and addressing of one wave's part of a split.
+// Lane layout and per-lane address offsets (the same for every split).
 struct Lanes {
   int lane, kg, kc, vg, hb, hg, dl;
   bool dup0;
+  uint32_t kc16, vc16;   // lane's 16-byte chunk within a K / V row
+  uint32_t koff, voff;   // lane's chunk within a row group: kg*rsb + kc*16, vg*rsb + vc*16
 };
 
 // Issue the 16-byte direct-to-LDS loads of one tile (K rows, then V rows) into
@@ -488,18 +492,18 @@ __device__ __forceinline__ void issue_tile(const SplitCtx& c, const Lanes& ln, i
       const char* rb = c.kh + (uint64_t)(uint32_t)blk * c.blk_bytes + (uint32_t)(tr & bmask) * c.rsb;
 #pragma unroll
       for (int i = 0; i < G::KCH; ++i)
-        dma16s(rb + i * G::LPT_K * 16, c.koff, base + (r * G::KCH + i) * 1024);
+        dma16s(rb + i * G::LPT_K * 16, ln.koff, base + (r * G::KCH + i) * 1024);
     }
 #pragma unroll
     for (int r = 0; r < G::RV; ++r) {
       const int tr = tb + r * G::TPW_V;
       const int blk = __builtin_amdgcn_readfirstlane(pick(ti, (r * G::TPW_V) >> c.bshift));
       const char* rb = c.vh + (uint64_t)(uint32_t)blk * c.blk_bytes + (uint32_t)(tr & bmask) * c.rsb;
-      dma16s(rb, c.voff, base + (G::RK * G::KCH + r) * 1024);
+      dma16s(rb, ln.voff, base + (G::RK * G::KCH + r) * 1024);
     }
     return;
   }
-  auto row = [&](int tt, const char* lb, const char* zb) -> const char* {
+  auto row = [&](int tt, const char* lb, const char* zb, const char* nb) -> const char* {
     int blk;
     bool ok = tt < c.t1;
     if (UNI) {
@@ -510,17 +514,21 @@ __device__ __forceinline__ void issue_tile(const SplitCtx& c, const Lanes& ln, i
       blk = ok ? c.tbl[(tt >> c.bshift) - c.tbl_base] : -1;
       ok = blk >= 0;
     }
+    if (ok && tt == c.tnew) return nb;
     return ok ? lb + (uint64_t)(uint32_t)blk * c.blk_bytes + (uint32_t)(tt & bmask) * c.rsb : zb;
   };
 #pragma unroll
   for (int r = 0; r < G::RK; ++r) {
-    const char* p = row(tb + r * G::TPW_K + ln.kg, c.kb, c.kz);
+    const char* p = row(tb + r * G::TPW_K + ln.kg, c.kh + ln.kc16,
+                        reinterpret_cast<const char*>(g_zero_row) + ln.kc16, c.knew + ln.kc16);
 #pragma unroll
     for (int i = 0; i < G::KCH; ++i) dma16(p + i * G::LPT_K * 16, base + (r * G::KCH + i) * 1024);
   }
 #pragma unroll
   for (int r = 0; r < G::RV; ++r)
-    dma16(row(tb + r * G::TPW_V + ln.vg, c.vb, c.vz), base + (G::RK * G::KCH + r) * 1024);
+    dma16(row(tb + r * G::TPW_V + ln.vg, c.vh + ln.vc16,
+              reinterpret_cast<const char*>(g_zero_row) + ln.vc16, c.vnew + ln.vc16),
+          base + (G::RK * G::KCH + r) * 1024);
 }
 
 template <typename T, int HD, int REP, bool UNI>
@@ -587,7 +595,7 @@ __device__ __forceinline__ void wave_tiles(const SplitCtx& c, const Lanes& ln,
 #pragma unroll
     for (int i = 0; i < G::NID; ++i) ti.id[i] = 0;
     ti.ok = 0;
-    ti.masked = any_bad || tb + G::TILE > c.t1;
+    ti.masked = any_bad || tb + G::TILE > c.t1 || (c.tnew >= tb && c.tnew < tb + G::TILE);
     return ti;
   };
   if (UNI) {
@@ -653,9 +661,6 @@ struct Lds {
     return G::TPW_K <= (1 << bshift) && G::TPW_V <= (1 << bshift);
   }
 };
-
-// 16-byte pieces of dead tokens are read from here (longest row: fp32 x 256).
-__device__ __attribute__((aligned(16))) unsigned char g_zero_row[1024];
 
 template <typename T, int HD, int REP>
 __global__ void __launch_bounds__(kThreads)
@@ -727,6 +732,30 @@ decode_partials_kernel(DecodeArgs a) {
   c.num_blocks = a.num_blocks;
   c.t1 = t1;
   c.scale_log2 = a.scale_log2;
+  c.tnew = -1;
+  c.knew = c.vnew = nullptr;
+  if (a.k_new && j == nsplit - 1) {
+    // fused step: this workgroup owns the new token of KV head g
+    const int tn = ctx - 1;
+    const size_t row_off = ((size_t)s * a.num_kv_heads + g) * HD * G::ISZ;
+    c.tnew = tn;
+    c.knew = reinterpret_cast<const char*>(a.k_new) + row_off;
+    c.vnew = reinterpret_cast<const char*>(a.v_new) + row_off;
+    const int id = c.trow[tn >> bshift];
+    if ((unsigned)id < (unsigned)a.num_blocks) {
+      constexpr int CH = G::ROWB / 16;   // 16-byte chunks of one head's row
+      const size_t dst = ((size_t)(uint32_t)id << bshift | (uint32_t)(tn & ((1 << bshift) - 1))) *
+                             ((size_t)a.num_kv_heads * G::ROWB) +
+                         (size_t)g * G::ROWB;
+      if (tid < 2 * CH) {
+        const bool isv = tid >= CH;
+        const int ch = isv ? tid - CH : tid;
+        const uint4 v = *reinterpret_cast<const uint4*>((isv ? c.vnew : c.knew) + ch * 16);
+        char* pool = reinterpret_cast<char*>(const_cast<void*>(isv ? a.v_pool : a.k_pool));
+        *reinterpret_cast<uint4*>(pool + dst + ch * 16) = v;
+      }
+    }
+  }
 
   // ---- per-lane path: stage this split's block ids in LDS (invalid -> -1)
   int any_bad = 0;
@@ -765,14 +794,12 @@ decode_partials_kernel(DecodeArgs a) {
     const size_t head_off = (size_t)g * HD * G::ISZ;
     c.kh = reinterpret_cast<const char*>(a.k_pool) + head_off;
     c.vh = reinterpret_cast<const char*>(a.v_pool) + head_off;
-    c.kb = c.kh + ln.kc * 16;
-    c.vb = c.vh + vc * 16;
-    c.kz = reinterpret_cast<const char*>(g_zero_row) + ln.kc * 16;
-    c.vz = reinterpret_cast<const char*>(g_zero_row) + vc * 16;
     c.rsb = (uint32_t)a.num_kv_heads * HD * G::ISZ;
     c.blk_bytes = c.rsb << bshift;
-    c.koff = (uint32_t)ln.kg * c.rsb + ln.kc * 16;
-    c.voff = (uint32_t)ln.vg * c.rsb + vc * 16;
+    ln.kc16 = (uint32_t)ln.kc * 16;
+    ln.vc16 = (uint32_t)vc * 16;
+    ln.koff = (uint32_t)ln.kg * c.rsb + ln.kc16;
+    ln.voff = (uint32_t)ln.vg * c.rsb + ln.vc16;
   }
 
   WaveState<T, HD, REP> st;

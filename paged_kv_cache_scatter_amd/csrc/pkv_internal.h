@@ -52,6 +52,12 @@ struct DecodeArgs {
   // sequence s (n_s rows) attends positions 0 .. ctx_s - n_s + (r - cu_q[s]).
   const int32_t* cu_q;
   int32_t total_q;
+  // Fused decode step: when k_new is set, the new token of sequence s (rows
+  // k_new/v_new[s] : [Hkv, hd]) sits at position ctx_s - 1; the workgroup of the
+  // sequence's last split writes its head's rows into the pool slot and every
+  // read of that position takes them from k_new/v_new.
+  const void* k_new;
+  const void* v_new;
 };
 constexpr int kRowGridZ = 32768;   // rows per grid z-extent in prefill-row launches
 // Token tile per wave for a row of `row_bytes` (K or V of one KV head).

@@ -413,6 +413,8 @@ pkv_status launch_rows(const PrefillArgs& p, int dtype, int head_dim, int rep, h
   a.scale_log2 = p.scale_log2;
   a.cu_q = p.cu_q;
   a.total_q = p.total_q;
+  a.k_new = nullptr;
+  a.v_new = nullptr;
   return launch_decode_partials(a, dtype, head_dim, rep, st);
 }
 
