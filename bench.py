@@ -6,6 +6,9 @@ One step = the whole path for one layer of a decode batch:
   2. the KV write of those rows into the pool,
   3. split-K paged decode attention over every sequence's whole context,
   4. the merge of split partials.
+The timed step is the library's fused form (pkv_decode_step: 1-3 in one
+launch, then the merge); the same step with the write as separate launches
+(pkv_slot_mapping + pkv_write + pkv_decode) is reported beside it.
 Default workload: the LLaMA-2-70B per-layer shape (64 sequences, context
 lengths log-uniform in [512, 8192), 64 query / 8 KV heads, head_dim 128,
 bf16, 16-token blocks scattered over a 32,769-block pool). The timed loop
@@ -62,10 +65,12 @@ def workload_label(wl) -> str:
 
 
 class Step:
-    """Device state for one decode step of workload ``wl``."""
+    """Device state for one decode step of workload ``wl`` (fused: the write of
+    the new tokens inside the decode launch; else separate launches)."""
 
-    def __init__(self, wl, partition: int = 0):
+    def __init__(self, wl, partition: int = 0, fused: bool = True):
         self.wl = wl
+        self.fused = fused
         dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
         self.k_pool = torch.zeros(wl.pool_shape, dtype=dt, device=DEV)
         self.v_pool = torch.zeros(wl.pool_shape, dtype=dt, device=DEV)
@@ -79,6 +84,9 @@ class Step:
         self.s_tabs, self.s_first, self.s_cu = to_dev(s_tabs), to_dev(s_first), to_dev(s_cu)
         self.n_new = int(s_cu[-1])
         self.k_new, self.v_new = to_dev(wl.k_rows[s_rows]), to_dev(wl.v_rows[s_rows])
+        # one row per sequence for the fused step (an empty sequence's row is unused)
+        rows_s = np.array([r[-1] if len(r) else 0 for r in wl.seq_rows], dtype=np.int64)
+        self.k_step, self.v_step = to_dev(wl.k_rows[rows_s]), to_dev(wl.v_rows[rows_s])
         self.slots = torch.empty(self.n_new, dtype=torch.int32, device=DEV)
         self.q = to_dev(wl.q)
         self.out = torch.empty_like(self.q)
@@ -94,6 +102,18 @@ class Step:
 
     def run(self, ev_a=None, ev_b=None):
         wl = self.wl
+        if self.fused:
+            if ev_a is not None:
+                ev_a.record()
+            pkv.decode_step(self.q, self.k_step, self.v_step, self.k_pool, self.v_pool,
+                            self.tables, self.ctx, wl.scale, self.max_ctx, out=self.out,
+                            partition=self.partition, workspace=self.ws, phase="partials")
+            if ev_b is not None:
+                ev_b.record()
+            pkv.decode(self.q, self.k_pool, self.v_pool, self.tables, self.ctx, wl.scale,
+                       self.max_ctx, out=self.out, partition=self.partition, workspace=self.ws,
+                       phase="reduce")
+            return
         pkv.slot_mapping(self.s_tabs, self.s_first, self.s_cu, self.n_new, wl.block_size,
                          wl.num_blocks, out=self.slots)
         pkv.write(self.k_new, self.v_new, self.slots, self.k_pool, self.v_pool)
@@ -350,17 +370,29 @@ def main():
         "config": {"workload": workload_label(wl), "num_seqs": wl.num_seqs,
                    "total_context_tokens": wl.total_ctx, "kv_bytes_per_step": kvb,
                    "partition_tokens": step.partition,
-                   "step": "slot mapping + KV write of 1 token/seq + decode partials + merge"},
+                   "step": "pkv_decode_step (slot mapping + KV write of 1 token/seq + decode "
+                           "partials, one launch) + merge"},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(wl.num_seqs / (ms_step * 1e-3), 1),
         "context_tokens_per_s": round(wl.total_ctx / (ms_step * 1e-3), 1),
-        "roofline": {"bound": "hbm", "kernel": "decode_partials_kernel",
+        "roofline": {"bound": "hbm", "kernel": "decode_partials_kernel (fused step)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel_ms": round(ms_kernel, 5),
                      "algorithmic_bytes_per_launch": kvb},
     }
     if not args.no_extra:
+        del step
+        torch.cuda.empty_cache()
+        print("[bench] the same step with separate write launches", file=sys.stderr, flush=True)
+        sep = Step(wl, args.partition, fused=False)
+        ms_sep, ms_sep_k = time_steps(sep, args.steps, args.warmup)
+        res["separate_write_step"] = {
+            "step": "pkv_slot_mapping + pkv_write + pkv_decode partials + merge",
+            "ms_per_step": round(ms_sep, 5), "value": round(kvb / (ms_sep * 1e-3) / 1e9, 1),
+            "unit": "GB/s", "decode_partials_ms": round(ms_sep_k, 5)}
+        del sep
+        torch.cuda.empty_cache()
         extra = {}
         for cfg in (3, 4):
             if cfg == args.config:
