@@ -66,7 +66,9 @@ typedef enum pkv_status {
                               group size, block size)                             */
   PKV_ERR_WORKSPACE = 5,   /* decode workspace missing or too small              */
   PKV_ERR_HIP = 6,         /* the HIP runtime rejected a launch                   */
-  PKV_ERR_ALIGN = 7        /* a pointer is not 16-byte aligned where required     */
+  PKV_ERR_ALIGN = 7,       /* a pointer is not 16-byte aligned where required     */
+  PKV_ERR_CAPACITY = 8     /* a planned pool cannot hold one request of the
+                              required length                                    */
 } pkv_status;
 
 typedef enum pkv_dtype { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
@@ -241,6 +243,37 @@ pkv_status pkv_prefill(const void* q, const int32_t* cu_q, int32_t num_seqs,
                        int32_t max_blocks_per_seq, const int32_t* context_lens,
                        int32_t max_context_len, float scale, void* out,
                        void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Pool sizing ([D38] "Why it matters"; host arithmetic, no device access).
+ *
+ * pkv_block_bytes: bytes of one block of a layered pool, K and V for every
+ * layer and KV head: 2 * num_layers * block_size * num_kv_heads * head_dim *
+ * itemsize (512 KiB for Llama-3.2-1B at block 16 in bf16; use the KV head
+ * count, not the attention head count). Returns 0 if an argument is < 1.
+ *
+ * pkv_plan_pool: the number of blocks a device holds after the weights are
+ * resident,
+ *   budget = free_bytes - (1 - utilization) * total_bytes - activation_bytes,
+ *   *num_blocks = floor(budget / block_bytes),
+ * where free_bytes is what the driver reports free with the weights loaded,
+ * utilization the fraction of the whole device the server may use, and
+ * activation_bytes the transient reserve of the largest forward. Also
+ * *requests_at_max_len = floor(*num_blocks / ceil(max_model_len / block_size))
+ * (full-length requests the pool holds, not clamped by any slot count).
+ * Returns PKV_ERR_CAPACITY, and still fills both outputs, when the pool holds
+ * less than one request of max_model_len tokens ([D38]: a pool that cannot
+ * hold one request refuses everything); pkv_last_error() then names the
+ * longest length it could serve. PKV_ERR_SHAPE for negative sizes, a
+ * utilization outside (0, 1], block_bytes < 1 or block_size < 1.
+ * ------------------------------------------------------------------------- */
+int64_t pkv_block_bytes(int32_t num_layers, int32_t block_size, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t itemsize);
+
+pkv_status pkv_plan_pool(int64_t free_bytes, int64_t total_bytes, double utilization,
+                         int64_t activation_bytes, int64_t block_bytes, int32_t block_size,
+                         int32_t max_model_len, int64_t* num_blocks,
+                         int64_t* requests_at_max_len);
 
 /* Human-readable name of a status. Never NULL. */
 const char* pkv_status_string(pkv_status status);

@@ -12,11 +12,13 @@ from ._binding import (  # noqa: F401
     PkvError,
     PoolDesc,
     abi_version,
+    block_bytes,
     decode,
     decode_step,
     decode_partition,
     decode_workspace_bytes,
     load,
+    plan_pool,
     pool_desc,
     prefill,
     slot_mapping,

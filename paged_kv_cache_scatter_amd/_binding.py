@@ -22,13 +22,14 @@ _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
 
 _STATUS = {0: "PKV_OK", 1: "PKV_ERR_NULL", 2: "PKV_ERR_DTYPE", 3: "PKV_ERR_SHAPE",
            4: "PKV_ERR_UNSUPPORTED", 5: "PKV_ERR_WORKSPACE", 6: "PKV_ERR_HIP",
-           7: "PKV_ERR_ALIGN"}
+           7: "PKV_ERR_ALIGN", 8: "PKV_ERR_CAPACITY"}
 
 # Every symbol include/pkv.h declares.
 EXPORTS = ("pkv_slot_mapping", "pkv_write", "pkv_decode_partition",
            "pkv_decode_workspace_bytes", "pkv_decode", "pkv_decode_partials",
            "pkv_decode_reduce", "pkv_decode_step", "pkv_decode_step_partials", "pkv_prefill",
-           "pkv_status_string", "pkv_last_error", "pkv_abi_version")
+           "pkv_block_bytes", "pkv_plan_pool", "pkv_status_string", "pkv_last_error",
+           "pkv_abi_version")
 
 
 class PkvError(RuntimeError):
@@ -82,6 +83,12 @@ def load(path: str | None = None):
     lib.pkv_prefill.argtypes = [_P, _P, _I, _I, _I, _I, _P, _P, ctypes.POINTER(PoolDesc), _P,
                                 _I, _P, _I, ctypes.c_float, _P, _P]
     lib.pkv_prefill.restype = ctypes.c_int
+    lib.pkv_block_bytes.argtypes = [_I, _I, _I, _I, _I]
+    lib.pkv_block_bytes.restype = ctypes.c_int64
+    lib.pkv_plan_pool.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_double, ctypes.c_int64,
+                                  ctypes.c_int64, _I, _I, ctypes.POINTER(ctypes.c_int64),
+                                  ctypes.POINTER(ctypes.c_int64)]
+    lib.pkv_plan_pool.restype = ctypes.c_int
     lib.pkv_status_string.argtypes = [ctypes.c_int]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_last_error.argtypes = []
@@ -292,3 +299,22 @@ def prefill(q: torch.Tensor, cu_q: torch.Tensor, k_pool: torch.Tensor, v_pool: t
 
 def abi_version() -> int:
     return int(load().pkv_abi_version())
+
+
+# ---------------------------------------------------------------- pool sizing
+def block_bytes(num_layers: int, block_size: int, num_kv_heads: int, head_dim: int,
+                itemsize: int) -> int:
+    """Bytes of one block of a layered K/V pool (0 if an argument is < 1)."""
+    return int(load().pkv_block_bytes(int(num_layers), int(block_size), int(num_kv_heads),
+                                      int(head_dim), int(itemsize)))
+
+
+def plan_pool(free_bytes: int, total_bytes: int, utilization: float, activation_bytes: int,
+              block_bytes: int, block_size: int, max_model_len: int):
+    """(num_blocks, requests_at_max_len) for a device; raises PkvError
+    (PKV_ERR_CAPACITY) if the pool cannot hold one request of max_model_len."""
+    nb, nr = ctypes.c_int64(), ctypes.c_int64()
+    _check(load().pkv_plan_pool(int(free_bytes), int(total_bytes), float(utilization),
+                                int(activation_bytes), int(block_bytes), int(block_size),
+                                int(max_model_len), ctypes.byref(nb), ctypes.byref(nr)))
+    return int(nb.value), int(nr.value)

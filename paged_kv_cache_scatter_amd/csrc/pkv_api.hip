@@ -489,6 +489,45 @@ pkv_status pkv_prefill(const void* q, const int32_t* cu_q, int32_t num_seqs, int
                         reinterpret_cast<hipStream_t>(stream));
 }
 
+int64_t pkv_block_bytes(int32_t num_layers, int32_t block_size, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t itemsize) {
+  if (num_layers < 1 || block_size < 1 || num_kv_heads < 1 || head_dim < 1 || itemsize < 1)
+    return 0;
+  return (int64_t)2 * num_layers * block_size * num_kv_heads * head_dim * itemsize;
+}
+
+pkv_status pkv_plan_pool(int64_t free_bytes, int64_t total_bytes, double utilization,
+                         int64_t activation_bytes, int64_t block_bytes, int32_t block_size,
+                         int32_t max_model_len, int64_t* num_blocks,
+                         int64_t* requests_at_max_len) {
+  if (!num_blocks || !requests_at_max_len) {
+    set_error("num_blocks and requests_at_max_len must not be NULL");
+    return PKV_ERR_NULL;
+  }
+  if (free_bytes < 0 || total_bytes < 0 || activation_bytes < 0 || block_bytes < 1 ||
+      block_size < 1 || max_model_len < 0 || !(utilization > 0.0 && utilization <= 1.0)) {
+    set_error("bad sizes: free %lld, total %lld, utilization %g, activation %lld, block_bytes "
+              "%lld, block_size %d, max_model_len %d", (long long)free_bytes,
+              (long long)total_bytes, utilization, (long long)activation_bytes,
+              (long long)block_bytes, block_size, max_model_len);
+    return PKV_ERR_SHAPE;
+  }
+  // reserve = (1 - utilization) * total, rounded up to whole bytes
+  const long double reserve = (1.0L - (long double)utilization) * (long double)total_bytes;
+  const long double budget = (long double)free_bytes - reserve - (long double)activation_bytes;
+  const int64_t blocks = budget > 0 ? (int64_t)(budget / (long double)block_bytes) : 0;
+  const int64_t per_req = ((int64_t)max_model_len + block_size - 1) / block_size;
+  *num_blocks = blocks;
+  *requests_at_max_len = per_req > 0 ? blocks / per_req : 0;
+  if (per_req > blocks) {
+    set_error("a pool of %lld blocks cannot hold one request of %d tokens (%lld blocks); the "
+              "longest it could serve is %lld tokens", (long long)blocks, max_model_len,
+              (long long)per_req, (long long)(blocks * block_size));
+    return PKV_ERR_CAPACITY;
+  }
+  return PKV_OK;
+}
+
 const char* pkv_status_string(pkv_status s) {
   switch (s) {
     case PKV_OK: return "PKV_OK";
@@ -499,6 +538,7 @@ const char* pkv_status_string(pkv_status s) {
     case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE";
     case PKV_ERR_HIP: return "PKV_ERR_HIP";
     case PKV_ERR_ALIGN: return "PKV_ERR_ALIGN";
+    case PKV_ERR_CAPACITY: return "PKV_ERR_CAPACITY";
   }
   return "PKV_ERR_UNKNOWN";
 }
