@@ -17,6 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpkv.so")
 SOURCES = ["pkv_api.hip", "pkv_write.hip", "pkv_decode.hip", "pkv_prefill.hip"]
+HOST_SOURCES = ["pkv_sched.cpp"]   # host-only C++ (the scheduler above the kernels)
 ARCH = "gfx950"
 
 # Packed-fp32 VALU ops are switched off for the device code; hipcc's host pass
@@ -31,6 +32,13 @@ def hipcc() -> str:
         if cand and os.path.exists(cand):
             return cand
     raise RuntimeError("hipcc not found (ROCm is required to build libpkv.so)")
+
+
+def cxx() -> str:
+    for cand in (os.environ.get("CXX"), shutil.which("g++"), shutil.which("c++")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("no host C++ compiler (g++) found")
 
 
 def _run(cmd, verbose):
@@ -51,6 +59,11 @@ def build(verbose: bool = False) -> str:
     os.makedirs(objdir, exist_ok=True)
     objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in SOURCES]
     cmds = [[cc, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    for s in HOST_SOURCES:
+        o = os.path.join(objdir, s.replace(".cpp", ".o"))
+        cmds.append([cxx(), "-O2", "-std=c++17", "-fPIC", "-Wall", "-c", os.path.join(CSRC, s),
+                     "-o", o])
+        objs.append(o)
     workers = min(len(cmds), max(1, (os.cpu_count() or 4)))
     with ThreadPoolExecutor(max_workers=workers) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))

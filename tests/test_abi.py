@@ -1,5 +1,5 @@
-"""The C ABI without a GPU: the library loads, exports what include/pkv.h
-declares, and rejects bad arguments before touching the GPU."""
+"""The C ABI without a GPU: the library loads, exports what include/*.h
+declare, and rejects bad arguments before touching the GPU."""
 
 import ctypes
 import os
@@ -7,10 +7,14 @@ import re
 
 import pytest
 
+import glob
+
 import paged_kv_cache_scatter_amd as pkv
 from paged_kv_cache_scatter_amd._binding import PoolDesc
+from paged_kv_cache_scatter_amd.sched import SCHED_EXPORTS
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "pkv.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
+HEADER = os.path.join(INCLUDE, "pkv.h")
 
 
 @pytest.fixture(scope="module")
@@ -18,18 +22,25 @@ def lib():
     return pkv.load()
 
 
-def _declared():
-    src = open(HEADER).read()
+def _declared(path):
+    src = open(path).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(pkv_[a-z_0-9]+)\s*\(", src)))
 
 
 def test_every_declared_symbol_is_exported(lib):
-    names = _declared()
-    assert len(names) >= 11
-    for n in names:
-        assert hasattr(lib, n), n
-    assert sorted(pkv.EXPORTS) == names
+    headers = sorted(glob.glob(os.path.join(INCLUDE, "*.h")))
+    assert len(headers) >= 2
+    every = set()
+    for h in headers:
+        names = _declared(h)
+        assert names, h
+        for n in names:
+            assert hasattr(lib, n), f"{n} ({os.path.basename(h)})"
+        every |= set(names)
+    assert sorted(pkv.EXPORTS) == _declared(HEADER)
+    assert sorted(SCHED_EXPORTS) == _declared(os.path.join(INCLUDE, "pkv_sched.h"))
+    assert every == set(pkv.EXPORTS) | set(SCHED_EXPORTS)
 
 
 def test_abi_version_and_strings(lib):

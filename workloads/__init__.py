@@ -7,3 +7,4 @@ oracle (``oracle/``) and the HIP path consume what it returns.
 """
 
 from .gen import CONFIGS, Workload, kv_bytes, make_custom, make_workload, poison_pool  # noqa: F401
+from .engine import TokenRows, engine_requests  # noqa: F401
