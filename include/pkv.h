@@ -222,6 +222,61 @@ pkv_status pkv_decode_step_partials(const void* q, const void* k_new, const void
                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * pkv_decode_shared -- paged decode for groups of sequences whose block tables
+ * begin with the same blocks (a shared prompt: [NV] "Prefix caching", where
+ * later users reuse the first user's full prompt blocks; [NV] "Where the time
+ * went", where per-user gathers read a 500-token shared prompt once per user
+ * and step; [NV] "Next steps" item 3, reading shared blocks once; [MV] "Key
+ * Takeaways" item 6, prefix sharing).
+ *
+ * The result is that of pkv_decode with the same arguments (same definition;
+ * only the summation order differs). Group i holds the consecutive sequences
+ * group_start[i] .. group_start[i+1]-1 and shares its first prefix_lens[i]
+ * tokens, rounded down to whole blocks and capped at max_prefix_len and the
+ * table reach; call that P_i. The caller guarantees that the first P_i /
+ * block_size table entries of every member are the same blocks (the kernels
+ * read them from the group's first member). Each member s attends its
+ * positions 0 .. min(ctx_s, P_i) - 1 through a shared pass that reads every
+ * shared K/V row once for all members and heads of the group (matrix cores,
+ * fp32 accumulation; bf16 probabilities are rounded to bf16 for the PV
+ * product, as in pkv_prefill), and its positions min(ctx_s, P_i) .. ctx_s - 1
+ * through the decode kernel; the split partials of both are merged as in
+ * pkv_decode.
+ *
+ * group_start: device int32 [num_groups + 1], non-decreasing, group_start[0]
+ *   == 0, group_start[num_groups] == num_seqs (values are clamped into
+ *   [0, num_seqs]; sequences outside every group are not valid input).
+ * prefix_lens: device int32 [num_groups], tokens.
+ * max_group_size >= the member count of every group; max_prefix_len >= every
+ *   prefix_lens[i] (and <= max_context_len); max_tail_len >= ctx_s - min(ctx_s,
+ *   P_i) for every s, or < 0 for max_context_len (positions past that bound
+ *   are not attended). partition: tokens per tail split (0 = auto from
+ *   max_tail_len), as in pkv_decode.
+ * workspace: pkv_decode_shared_workspace_bytes(...) bytes (device, 16-byte
+ *   aligned); 0 when no shared pass and no split is needed.
+ * With num_groups == 0, max_prefix_len < block_size, or a shape the shared
+ * pass does not compile (it covers bf16 and fp32 pools, head_dim 64 and 128,
+ * group size 1..8), the call is exactly pkv_decode. Errors are those of
+ * pkv_decode, plus PKV_ERR_SHAPE for inconsistent group sizes and
+ * PKV_ERR_NULL for a NULL group_start / prefix_lens when num_groups > 0.
+ * ------------------------------------------------------------------------- */
+size_t pkv_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                         int32_t max_context_len, int32_t num_groups,
+                                         int32_t max_group_size, int32_t max_prefix_len,
+                                         int32_t max_tail_len, int32_t partition,
+                                         const pkv_pool_desc* pool);
+
+pkv_status pkv_decode_shared(const void* q, int32_t num_seqs, int32_t num_q_heads,
+                             const void* k_pool, const void* v_pool,
+                             const pkv_pool_desc* pool, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens,
+                             int32_t max_context_len, const int32_t* group_start,
+                             const int32_t* prefix_lens, int32_t num_groups,
+                             int32_t max_group_size, int32_t max_prefix_len,
+                             int32_t max_tail_len, float scale, int32_t partition, void* out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * pkv_prefill -- causal attention of a chunk of query rows over the pool
  * ([MV] section 4: scores + full((T,T), -inf).triu(1), softmax, weighted V).
  *
@@ -230,11 +285,12 @@ pkv_status pkv_decode_step_partials(const void* q, const void* k_new, const void
  * sequence's positions 0..a through its block table (its own K/V must already
  * be in the pool: write, then attend). Rows with a < 0 are zero.
  * cu_q: device int32 [num_seqs+1], non-decreasing from 0, cu_q[num_seqs] ==
- * total_q_rows; max_q_len >= every n_s. bf16 pools with head_dim 64 or 128
- * and at most 2048 table entries per sequence in reach (min(max_context_len,
- * max_blocks_per_seq * block_size) / block_size) use bf16 matrix cores (fp32
- * accumulation, probabilities rounded to bf16 for the PV product); other
- * cases run each row as a one-split decode (fp32 pools in fp32 throughout).
+ * total_q_rows; max_q_len >= every n_s. Pools with head_dim 64 or 128 and at
+ * most 2048 table entries per sequence in reach (min(max_context_len,
+ * max_blocks_per_seq * block_size) / block_size) use matrix cores: bf16 pools
+ * bf16 products with fp32 accumulation, probabilities rounded to bf16 for the
+ * PV product; fp32 pools fp32 products throughout. Other cases run each row as
+ * a one-split decode.
  * ------------------------------------------------------------------------- */
 pkv_status pkv_prefill(const void* q, const int32_t* cu_q, int32_t num_seqs,
                        int32_t num_q_heads, int32_t max_q_len, int32_t total_q_rows,

@@ -14,6 +14,8 @@ from ._binding import (  # noqa: F401
     abi_version,
     block_bytes,
     decode,
+    decode_shared,
+    decode_shared_workspace_bytes,
     decode_step,
     decode_partition,
     decode_workspace_bytes,

@@ -27,7 +27,8 @@ _STATUS = {0: "PKV_OK", 1: "PKV_ERR_NULL", 2: "PKV_ERR_DTYPE", 3: "PKV_ERR_SHAPE
 # Every symbol include/pkv.h declares.
 EXPORTS = ("pkv_slot_mapping", "pkv_write", "pkv_decode_partition",
            "pkv_decode_workspace_bytes", "pkv_decode", "pkv_decode_partials",
-           "pkv_decode_reduce", "pkv_decode_step", "pkv_decode_step_partials", "pkv_prefill",
+           "pkv_decode_reduce", "pkv_decode_step", "pkv_decode_step_partials",
+           "pkv_decode_shared_workspace_bytes", "pkv_decode_shared", "pkv_prefill",
            "pkv_block_bytes", "pkv_plan_pool", "pkv_status_string", "pkv_last_error",
            "pkv_abi_version")
 
@@ -80,6 +81,13 @@ def load(path: str | None = None):
         f = getattr(lib, name)
         f.argtypes = step_args
         f.restype = ctypes.c_int
+    lib.pkv_decode_shared_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I,
+                                                      ctypes.POINTER(PoolDesc)]
+    lib.pkv_decode_shared_workspace_bytes.restype = ctypes.c_size_t
+    lib.pkv_decode_shared.argtypes = [_P, _I, _I, _P, _P, ctypes.POINTER(PoolDesc), _P, _I, _P, _I,
+                                      _P, _P, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P,
+                                      ctypes.c_size_t, _P]
+    lib.pkv_decode_shared.restype = ctypes.c_int
     lib.pkv_prefill.argtypes = [_P, _P, _I, _I, _I, _I, _P, _P, ctypes.POINTER(PoolDesc), _P,
                                 _I, _P, _I, ctypes.c_float, _P, _P]
     lib.pkv_prefill.restype = ctypes.c_int
@@ -226,6 +234,60 @@ def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                                _ptr(block_tables), maxb, _ptr(context_lens),
                                int(max_context_len), float(scale), int(partition), _ptr(out),
                                _ptr(workspace), ws_bytes, _stream()))
+    return out
+
+
+def decode_shared_workspace_bytes(num_seqs: int, num_q_heads: int, max_context_len: int,
+                                  num_groups: int, max_group_size: int, max_prefix_len: int,
+                                  max_tail_len: int, k_pool: torch.Tensor,
+                                  partition: int = 0) -> int:
+    desc = pool_desc(k_pool)
+    return int(load().pkv_decode_shared_workspace_bytes(
+        int(num_seqs), int(num_q_heads), int(max_context_len), int(num_groups),
+        int(max_group_size), int(max_prefix_len), int(max_tail_len), int(partition),
+        ctypes.byref(desc)))
+
+
+def decode_shared(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                  block_tables: torch.Tensor, context_lens: torch.Tensor,
+                  group_start: torch.Tensor, prefix_lens: torch.Tensor, scale: float,
+                  max_context_len: int, max_group_size: int, max_prefix_len: int,
+                  max_tail_len: int = -1, out: torch.Tensor | None = None, partition: int = 0,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Paged decode where groups of consecutive sequences share the leading
+    blocks of their tables. ``group_start`` int32 [G+1] (members of group i are
+    sequences group_start[i] .. group_start[i+1]-1), ``prefix_lens`` int32 [G]
+    (shared tokens of each group). The ``max_*`` arguments are host-side bounds
+    (``max_tail_len`` < 0: ``max_context_len``). Same result as ``decode``."""
+    desc = _check_pools(k_pool, v_pool)
+    _dev(q, "q", k_pool.dtype)
+    _need(q.dim() == 3 and q.shape[2] == desc.head_dim, "q must be [S, Hq, head_dim]")
+    S, Hq, _ = q.shape
+    _dev(block_tables, "block_tables", torch.int32)
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == S,
+          "block_tables must be [S, max_blocks_per_seq]")
+    maxb = block_tables.shape[1]
+    _dev(context_lens, "context_lens", torch.int32, (S,))
+    _dev(group_start, "group_start", torch.int32)
+    _need(group_start.dim() == 1 and group_start.shape[0] >= 1, "group_start must be [G+1]")
+    G = group_start.shape[0] - 1
+    _dev(prefix_lens, "prefix_lens", torch.int32, (G,))
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype, q.shape)
+    need = decode_shared_workspace_bytes(S, Hq, max_context_len, G, max_group_size,
+                                         max_prefix_len, max_tail_len, k_pool, partition)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace", torch.uint8)
+        ws_bytes = workspace.numel()
+    _check(load().pkv_decode_shared(
+        _ptr(q), S, Hq, _ptr(k_pool), _ptr(v_pool), ctypes.byref(desc), _ptr(block_tables), maxb,
+        _ptr(context_lens), int(max_context_len), _ptr(group_start), _ptr(prefix_lens), G,
+        int(max_group_size), int(max_prefix_len), int(max_tail_len), float(scale),
+        int(partition), _ptr(out), _ptr(workspace), ws_bytes, _stream()))
     return out
 
 

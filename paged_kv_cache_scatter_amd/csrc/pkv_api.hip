@@ -146,17 +146,86 @@ pkv_status plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks
 
 enum class Phase { kBoth, kPartials, kReduce };
 
+// Caller's description of the shared-prefix groups (pkv_decode_shared).
+struct SharedIn {
+  const int32_t* group_start;
+  const int32_t* prefix_lens;
+  int32_t num_groups, max_group, max_prefix, max_tail;
+};
+
+// Shared-prefix plan: the tail splits (partition from the longest tail), then
+// the shared pass's key splits, sized for about two workgroups per CU.
+// sd->group_start stays NULL when the shared pass is not used (no groups, a
+// prefix shorter than a block, or a shape the matrix-core pass does not
+// compile); the plan is then plain decode.
+pkv_status plan_shared(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
+                       int32_t max_ctx, const SharedIn& in, int32_t partition,
+                       const pkv_pool_desc* pool, DecodePlan* plan, SharedDesc* sd) {
+  *sd = SharedDesc{};
+  pkv_status st = plan_decode(num_seqs, num_q_heads, max_blocks, max_ctx, partition, pool, plan);
+  if (st != PKV_OK) return st;
+  if (in.num_groups < 0 || in.num_groups > std::max(num_seqs, 0) || in.max_prefix < 0 ||
+      in.max_prefix > max_ctx || in.max_tail > max_ctx ||
+      (in.num_groups > 0 && (in.max_group < 1 || in.max_group > num_seqs))) {
+    set_error("bad shared-prefix sizes: num_groups %d, max_group_size %d, max_prefix_len %d, "
+              "max_tail_len %d (num_seqs %d, max_context_len %d)", in.num_groups, in.max_group,
+              in.max_prefix, in.max_tail, num_seqs, max_ctx);
+    return PKV_ERR_SHAPE;
+  }
+  const int bs = pool->block_size;
+  if (in.num_groups == 0 || in.max_prefix < bs ||
+      !shared_pass_supported(pool->dtype, pool->head_dim, plan->rep))
+    return PKV_OK;
+  const int tail = in.max_tail < 0 ? max_ctx : in.max_tail;
+  st = plan_decode(num_seqs, num_q_heads, max_blocks, tail, partition, pool, plan);
+  if (st != PKV_OK) return st;
+  const int64_t align = std::max(kSharedAlign, bs);
+  const int64_t row_tiles = ((int64_t)in.max_group * plan->rep + kSharedRows - 1) / kSharedRows;
+  const int64_t base = (int64_t)in.num_groups * pool->num_kv_heads * row_tiles;
+  const int64_t max_ks = (in.max_prefix + align - 1) / align;
+  const int64_t nks = std::min(std::max<int64_t>((2 * kNumCUs + base - 1) / base, 1), max_ks);
+  int64_t pp = ((in.max_prefix + nks - 1) / nks + align - 1) / align * align;
+  pp = std::min(pp, (int64_t)kSharedMaxTbl * bs / align * align);
+  const int64_t jp = (in.max_prefix + pp - 1) / pp;
+  const int64_t J = jp + plan->splits;
+  if (J > kMaxSplits) {
+    set_error("shared prefix: %lld splits per sequence exceed %d (raise partition)",
+              (long long)J, kMaxSplits);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  plan->splits = (int)J;
+  const size_t rows = (size_t)num_seqs * num_q_heads * J;
+  plan->ws_ml_bytes = ((rows * 2 * sizeof(float)) + 255) & ~(size_t)255;
+  plan->ws_bytes = plan->ws_ml_bytes + rows * (size_t)pool->head_dim * sizeof(float);
+  sd->group_start = in.group_start;
+  sd->prefix_lens = in.prefix_lens;
+  sd->num_groups = in.num_groups;
+  sd->max_prefix = in.max_prefix;
+  sd->prefix_part = (int)pp;
+  sd->prefix_slots = (int)jp;
+  return PKV_OK;
+}
+
 pkv_status decode_impl(Phase phase, const void* q, int32_t num_seqs, int32_t num_q_heads,
                        const void* k_pool, const void* v_pool, const pkv_pool_desc* pool,
                        const int32_t* block_tables, int32_t max_blocks,
                        const int32_t* context_lens, int32_t max_ctx, float scale,
                        int32_t partition, void* out, void* workspace, size_t workspace_bytes,
-                       void* stream, const void* k_new = nullptr, const void* v_new = nullptr) {
+                       void* stream, const void* k_new = nullptr, const void* v_new = nullptr,
+                       const SharedIn* shared = nullptr) {
   DecodePlan plan;
-  pkv_status st = plan_decode(num_seqs, num_q_heads, max_blocks, max_ctx, partition, pool,
-                              &plan);
+  SharedDesc sd{};
+  pkv_status st = shared ? plan_shared(num_seqs, num_q_heads, max_blocks, max_ctx, *shared,
+                                       partition, pool, &plan, &sd)
+                         : plan_decode(num_seqs, num_q_heads, max_blocks, max_ctx, partition,
+                                       pool, &plan);
   if (st != PKV_OK) return st;
   if (num_seqs == 0) return PKV_OK;
+  if (shared && shared->num_groups > 0 && (!shared->group_start || !shared->prefix_lens)) {
+    set_error("group_start %p or prefix_lens %p is NULL", (const void*)shared->group_start,
+              (const void*)shared->prefix_lens);
+    return PKV_ERR_NULL;
+  }
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out) {
     set_error("NULL pointer among q %p, k_pool %p, v_pool %p, block_tables %p, "
               "context_lens %p, out %p", q, k_pool, v_pool, (const void*)block_tables,
@@ -185,7 +254,7 @@ pkv_status decode_impl(Phase phase, const void* q, int32_t num_seqs, int32_t num
       return PKV_ERR_ALIGN;
     }
   }
-  DecodeArgs a;
+  DecodeArgs a{};
   a.q = q;
   a.k_pool = k_pool;
   a.v_pool = v_pool;
@@ -210,7 +279,32 @@ pkv_status decode_impl(Phase phase, const void* q, int32_t num_seqs, int32_t num
   a.total_q = 0;
   a.k_new = k_new;
   a.v_new = v_new;
+  a.sh = sd;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (sd.group_start && phase != Phase::kReduce) {
+    PrefillArgs p{};
+    p.q = q;
+    p.k_pool = k_pool;
+    p.v_pool = v_pool;
+    p.tables = block_tables;
+    p.ctx_lens = context_lens;
+    p.out = out;
+    p.num_seqs = num_seqs;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = pool->num_kv_heads;
+    p.num_blocks = pool->num_blocks;
+    p.block_shift = a.block_shift;
+    p.max_blocks = max_blocks;
+    p.max_ctx = max_ctx;
+    p.scale_log2 = a.scale_log2;
+    p.sh = sd;
+    p.ws_ml = a.ws_ml;
+    p.ws_o = a.ws_o;
+    p.num_slots = plan.splits;
+    p.max_group = shared->max_group;
+    st = launch_shared_pass(p, pool->dtype, pool->head_dim, plan.rep, s);
+    if (st != PKV_OK) return st;
+  }
   if (phase != Phase::kReduce) {
     st = launch_decode_partials(a, pool->dtype, pool->head_dim, plan.rep, s);
     if (st != PKV_OK) return st;
@@ -421,6 +515,39 @@ pkv_status pkv_decode_step_partials(const void* q, const void* k_new, const void
                      partition, out, workspace, workspace_bytes, stream, k_new, v_new);
 }
 
+size_t pkv_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                         int32_t max_context_len, int32_t num_groups,
+                                         int32_t max_group_size, int32_t max_prefix_len,
+                                         int32_t max_tail_len, int32_t partition,
+                                         const pkv_pool_desc* pool) {
+  if (!pool) return 0;
+  DecodePlan plan;
+  SharedDesc sd;
+  const int32_t maxb = pool->block_size > 0
+                           ? (max_context_len + pool->block_size - 1) / pool->block_size
+                           : 1;
+  const SharedIn in{nullptr, nullptr, num_groups, max_group_size, max_prefix_len, max_tail_len};
+  if (plan_shared(num_seqs, num_q_heads, maxb > 0 ? maxb : 1, max_context_len, in, partition,
+                  pool, &plan, &sd) != PKV_OK)
+    return 0;
+  return plan.ws_bytes;
+}
+
+pkv_status pkv_decode_shared(const void* q, int32_t num_seqs, int32_t num_q_heads,
+                             const void* k_pool, const void* v_pool, const pkv_pool_desc* pool,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t max_context_len,
+                             const int32_t* group_start, const int32_t* prefix_lens,
+                             int32_t num_groups, int32_t max_group_size, int32_t max_prefix_len,
+                             int32_t max_tail_len, float scale, int32_t partition, void* out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  const SharedIn in{group_start, prefix_lens, num_groups, max_group_size, max_prefix_len,
+                    max_tail_len};
+  return decode_impl(Phase::kBoth, q, num_seqs, num_q_heads, k_pool, v_pool, pool, block_tables,
+                     max_blocks_per_seq, context_lens, max_context_len, scale, partition, out,
+                     workspace, workspace_bytes, stream, nullptr, nullptr, &in);
+}
+
 pkv_status pkv_prefill(const void* q, const int32_t* cu_q, int32_t num_seqs, int32_t num_q_heads,
                        int32_t max_q_len, int32_t total_q_rows, const void* k_pool,
                        const void* v_pool, const pkv_pool_desc* pool,
@@ -467,7 +594,7 @@ pkv_status pkv_prefill(const void* q, const int32_t* cu_q, int32_t num_seqs, int
     set_error("num_seqs %d exceeds 65535", num_seqs);
     return PKV_ERR_UNSUPPORTED;
   }
-  PrefillArgs a;
+  PrefillArgs a{};
   a.q = q;
   a.cu_q = cu_q;
   a.k_pool = k_pool;

@@ -701,18 +701,29 @@ decode_partials_kernel(DecodeArgs a) {
     ctx = a.ctx_lens[s];
     ctx = ctx < 0 ? 0 : (ctx > lim ? lim : ctx);
   }
+  // Shared-prefix decode: the group's shared pass covers positions < start
+  // (nps partials in the leading slots); this kernel covers the tail.
+  int start = 0, nps = 0, slot0 = 0;
   const int P = a.partition;
-  const int nsplit = (ctx + P - 1) / P;
+  int nsplit;
+  if (a.sh.group_start) {
+    start = min(ctx, shared_len(a.sh, group_of(a.sh, s), lim, bshift));
+    nps = (start + a.sh.prefix_part - 1) / a.sh.prefix_part;
+    slot0 = a.sh.prefix_slots;
+    nsplit = min((ctx - start + P - 1) / P, a.num_splits - slot0);
+  } else {
+    nsplit = (ctx + P - 1) / P;
+  }
   const int hq0 = g * REP;
   T* out = reinterpret_cast<T*>(a.out) + ((size_t)qrow * a.num_q_heads + hq0) * HD;
 
   if (j >= nsplit) {
-    if (j == 0) {  // empty sequence: zeros
+    if (j == 0 && nps == 0) {  // empty sequence: zeros
       for (int i = tid; i < REP * HD; i += kThreads) out[i] = from_f32<T>(0.f);
     }
     return;
   }
-  const int t0 = j * P;
+  const int t0 = start + j * P;
   const int t1 = min(ctx, t0 + P);
   const bool uni = L::uniform(bshift);
 
@@ -865,10 +876,10 @@ decode_partials_kernel(DecodeArgs a) {
         O = fmaf(mv[2 * REP + h * HD + d], f, O);
       }
     }
-    if (nsplit == 1) {
+    if (nsplit == 1 && nps == 0) {
       out[h * HD + d] = from_f32<T>(Ls > 0.f ? O / Ls : 0.f);
     } else {
-      const size_t row = ((size_t)s * a.num_q_heads + hq0 + h) * J + j;
+      const size_t row = ((size_t)s * a.num_q_heads + hq0 + h) * J + slot0 + j;
       a.ws_o[row * HD + d] = O;
       if (d == 0) {
         a.ws_ml[row * 2] = M;
@@ -888,19 +899,30 @@ __global__ void __launch_bounds__(64) decode_reduce_kernel(DecodeArgs a, int hea
   int ctx = a.ctx_lens[s];
   ctx = ctx < 0 ? 0 : (ctx > lim ? lim : ctx);
   const int P = a.partition;
-  const int nsplit = (ctx + P - 1) / P;
-  if (nsplit <= 1) return;
   const int J = a.num_splits;
+  // partials: slots 0 .. nps-1 (shared pass), then slot0 .. slot0+nsplit-1
+  int nps = 0, slot0 = 0, nsplit;
+  if (a.sh.group_start) {
+    const int start = min(ctx, shared_len(a.sh, group_of(a.sh, s), lim, a.block_shift));
+    nps = (start + a.sh.prefix_part - 1) / a.sh.prefix_part;
+    slot0 = a.sh.prefix_slots;
+    nsplit = min((ctx - start + P - 1) / P, J - slot0);
+  } else {
+    nsplit = (ctx + P - 1) / P;
+  }
+  if (nps == 0 && nsplit <= 1) return;   // written by the partials kernel
+  const int n = nps + nsplit;
+  auto slot = [&](int i) { return i < nps ? i : slot0 + i - nps; };
   const size_t row0 = ((size_t)s * a.num_q_heads + h) * J;
   const float* ml = a.ws_ml + row0 * 2;
   float M = -INFINITY;
-  for (int j = lane; j < nsplit; j += 64) M = fmaxf(M, ml[2 * j]);
+  for (int i = lane; i < n; i += 64) M = fmaxf(M, ml[2 * slot(i)]);
   M = group_max<64>(M);
   float Ls = 0.f;
-  for (int j = lane; j < nsplit; j += 64) {
-    const float f = (M == -INFINITY) ? 0.f : fast_exp2(ml[2 * j] - M);
-    wts[j] = f;
-    Ls = fmaf(ml[2 * j + 1], f, Ls);
+  for (int i = lane; i < n; i += 64) {
+    const float f = (M == -INFINITY) ? 0.f : fast_exp2(ml[2 * slot(i)] - M);
+    wts[i] = f;
+    Ls = fmaf(ml[2 * slot(i) + 1], f, Ls);
   }
   Ls = group_sum<64>(Ls);
   __syncthreads();
@@ -908,7 +930,7 @@ __global__ void __launch_bounds__(64) decode_reduce_kernel(DecodeArgs a, int hea
   T* out = reinterpret_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + h) * head_dim;
   for (int d = lane; d < head_dim; d += 64) {
     float O = 0.f;
-    for (int j = 0; j < nsplit; ++j) O = fmaf(wts[j], po[(size_t)j * head_dim + d], O);
+    for (int i = 0; i < n; ++i) O = fmaf(wts[i], po[(size_t)slot(i) * head_dim + d], O);
     out[d] = from_f32<T>(Ls > 0.f ? O / Ls : 0.f);
   }
 }
@@ -918,7 +940,8 @@ template <typename T, int HD, int REP>
 pkv_status launch_split(const DecodeArgs& a, hipStream_t st) {
   using L = Lds<T, HD, REP>;
   const int lds = L::bytes(L::table_entries(a.partition, a.block_shift));
-  dim3 grid(a.num_kv_heads, a.num_seqs, a.num_splits);
+  // shared-prefix decode: the leading slots belong to the shared pass
+  dim3 grid(a.num_kv_heads, a.num_seqs, a.num_splits - a.sh.prefix_slots);
   if (a.cu_q) {
     const int z = a.total_q < kRowGridZ ? a.total_q : kRowGridZ;
     grid = dim3(a.num_kv_heads, (a.total_q + z - 1) / z, z);

@@ -36,6 +36,23 @@ struct WriteArgs {
 };
 void launch_write(const WriteArgs& a, bool vec16, int elem_bytes, hipStream_t st);
 
+// Shared-prefix decode: groups of consecutive sequences whose block tables
+// begin with the same blocks. Group i holds sequences group_start[i] ..
+// group_start[i+1]-1 and shares its first prefix_lens[i] tokens (rounded down
+// to whole blocks, capped by max_prefix and the table reach). A shared pass
+// attends each group's shared tokens once for all its members and leaves its
+// partials in workspace slots 0 .. prefix_slots-1 of every (sequence, head);
+// the decode kernel covers the rest of each context from the prefix boundary
+// into the following slots; the merge kernel combines both.
+struct SharedDesc {
+  const int32_t* group_start;   // nullptr: no sharing
+  const int32_t* prefix_lens;
+  int32_t num_groups;
+  int32_t max_prefix;           // tokens
+  int32_t prefix_part;          // tokens per shared-pass split
+  int32_t prefix_slots;         // slots per (sequence, head) given to the shared pass
+};
+
 struct DecodeArgs {
   const void* q;
   const void* k_pool;
@@ -58,6 +75,7 @@ struct DecodeArgs {
   // read of that position takes them from k_new/v_new.
   const void* k_new;
   const void* v_new;
+  SharedDesc sh;
 };
 constexpr int kRowGridZ = 32768;   // rows per grid z-extent in prefill-row launches
 // Token tile per wave for a row of `row_bytes` (K or V of one KV head).
@@ -80,10 +98,24 @@ struct PrefillArgs {
   int32_t num_seqs, num_q_heads, num_kv_heads, num_blocks;
   int32_t block_shift, max_blocks, max_ctx, max_q_len, total_q;
   float scale_log2;
+  // shared pass (sh.group_start set): partials go to the workspace, J slots
+  // per (sequence, head); q/out rows are sequences, cu_q is unused
+  SharedDesc sh;
+  float* ws_ml;
+  float* ws_o;
+  int32_t num_slots;
+  int32_t max_group;   // members of the largest group
 };
 bool prefill_supported(int dtype, int head_dim, int rep);
 pkv_status launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int rep,
                           hipStream_t st);
+// Shared pass of the shared-prefix decode (matrix cores).
+bool shared_pass_supported(int dtype, int head_dim, int rep);
+constexpr int kSharedAlign = 64;      // shared-pass split granularity (keys per LDS tile)
+constexpr int kSharedMaxTbl = 2048;   // table entries one shared-pass split may span
+constexpr int kSharedRows = 128;      // (member, head) rows per shared-pass workgroup
+pkv_status launch_shared_pass(const PrefillArgs& a, int dtype, int head_dim, int rep,
+                              hipStream_t st);
 
 }  // namespace pkv
 
@@ -148,6 +180,26 @@ __device__ __forceinline__ float group_max(float x) {
   if constexpr (W >= 32) x = fmaxf(x, swz_xor16(x));
   if constexpr (W >= 64) x = fmaxf(x, xor32(x));
   return x;
+}
+
+// Group of sequence s: the last i with group_start[i] <= s (0 if none).
+__device__ __forceinline__ int group_of(const SharedDesc& d, int s) {
+  int lo = 0, hi = d.num_groups;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (d.group_start[mid] <= s) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// Shared tokens of group i: whole blocks, within [0, min(max_prefix, lim)].
+__device__ __forceinline__ int shared_len(const SharedDesc& d, int i, int lim, int bshift) {
+  int p = d.prefix_lens[i];
+  p = p < 0 ? 0 : p;
+  p = p > d.max_prefix ? d.max_prefix : p;
+  p = p > lim ? lim : p;
+  return (p >> bshift) << bshift;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

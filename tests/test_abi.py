@@ -129,3 +129,44 @@ def test_binding_checks_shapes_before_calling():
     with pytest.raises(ValueError):
         pkv.write(k, k, torch.zeros(2, dtype=torch.int32), torch.zeros(1, 16, 1, 3),
                   torch.zeros(1, 16, 1, 3))
+
+
+def _shared_ws(lib, d, S=64, Hq=64, max_ctx=4096, G=1, mg=64, mp=2048, mt=2048, part=1024):
+    return lib.pkv_decode_shared_workspace_bytes(S, Hq, max_ctx, G, mg, mp, mt, part,
+                                                 ctypes.byref(d))
+
+
+def test_shared_prefix_plan(lib):
+    d = _desc(nb=32769, bs=16, hkv=8, hd=128)
+    # tails: 2 splits of 1024 tokens; shared pass: 1 group x 8 KV heads x 4 row
+    # tiles (64 members x 8 heads / 128 rows) = 32 units, so 16 key splits of
+    # 128 tokens for about two workgroups per CU
+    rows = 64 * 64 * (16 + 2)
+    assert _shared_ws(lib, d) == rows * 2 * 4 + rows * 128 * 4
+    # no groups, a prompt shorter than a block, an uncompiled head size: plain decode
+    plain = lib.pkv_decode_workspace_bytes(64, 64, 4096, 1024, ctypes.byref(d))
+    assert _shared_ws(lib, d, G=0) == plain
+    assert _shared_ws(lib, d, mp=15) == plain
+    d32 = _desc(nb=32769, bs=16, hkv=8, hd=32)
+    assert _shared_ws(lib, d32) == lib.pkv_decode_workspace_bytes(64, 64, 4096, 1024,
+                                                                  ctypes.byref(d32))
+    # the tail partition follows max_tail_len; < 0 means max_context_len
+    assert _shared_ws(lib, d, mt=-1) == 64 * 64 * (16 + 4) * (2 + 128) * 4
+    # inconsistent sizes give 0 bytes
+    for kw in (dict(mp=5000), dict(G=65), dict(mg=0), dict(mg=65), dict(mt=5000), dict(G=-1)):
+        assert _shared_ws(lib, d, **kw) == 0, kw
+
+
+def test_shared_prefix_argument_errors(lib):
+    d = _desc(nb=64, bs=16, hkv=8, hd=128)
+
+    def call(gs=16, pl=16, G=1, mg=4, mp=64, mt=-1, S=4, ws=16, wsb=1 << 30):
+        return lib.pkv_decode_shared(16, S, 64, 16, 16, ctypes.byref(d), 16, 8, 16, 100, gs, pl,
+                                     G, mg, mp, mt, 0.1, 0, 16, ws, wsb, None)
+    assert call(gs=None) == 1 and "NULL" in _err(lib)
+    assert call(pl=None) == 1
+    assert call(G=5) == 3 and "shared-prefix" in _err(lib)
+    assert call(mp=101) == 3
+    assert call(mg=0) == 3
+    assert call(ws=None, wsb=0) == 5 and "workspace" in _err(lib)
+    assert call(S=0, G=0, mg=0) == 0      # nothing to do

@@ -85,17 +85,19 @@ def _ref(pc, q_rows, cu, tables=None, ctx=None):
                           wl.context_lens if ctx is None else ctx, wl.scale, wl.dtype)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("hd", [64, 128])
-def test_prefill_matrix_core_variants(hd):
-    """bf16 chunks on every compiled group size: chunks spanning several query
-    tiles with ragged ends, a one-row chunk, and a chunk longer than its
-    context (leading rows zero); K/V ranges spanning several key tiles."""
+def test_prefill_matrix_core_variants(hd, dtype):
+    """Chunks on every compiled group size (bf16 and fp32 matrix cores):
+    chunks spanning several query tiles with ragged ends, a one-row chunk, and
+    a chunk longer than its context (leading rows zero); K/V ranges spanning
+    several key tiles."""
     lens = [150, 70, 33, 300, 1]
     qlens = [150, 20, 40, 130, 1]
     for rep in range(1, 9):
-        pc, cu, q_rows = _case(lens, qlens, "bf16", hd, rep, seed=rep)
-        got = out_f64(_run(pc, q_rows, cu, max(qlens)), "bf16")
-        check_close(got, _ref(pc, q_rows, cu), "bf16", f"hd={hd} rep={rep}")
+        pc, cu, q_rows = _case(lens, qlens, dtype, hd, rep, seed=rep)
+        got = out_f64(_run(pc, q_rows, cu, max(qlens)), dtype)
+        check_close(got, _ref(pc, q_rows, cu), dtype, f"hd={hd} rep={rep}")
         z0 = int(cu[2])
         assert not got[z0:z0 + 7].any(), "rows before position 0 are zero"
 
@@ -164,16 +166,28 @@ def test_prefill_long_table_takes_row_path():
 
 def test_prefill_one_row_equals_decode_row_path():
     """A one-row chunk at each sequence's last position is that sequence's
-    decode step. fp32 prefill runs the decode kernel's row mode, so with the
-    same single split the bits are identical."""
-    wl = make_workload(2, num_seqs=5)
+    decode step. head_dim 16 prefill runs the decode kernel's row mode, so with
+    the same single split the bits are identical."""
+    wl = make_workload(1)
     pc = PoolCase(wl)
     cu = np.arange(wl.num_seqs + 1, dtype=np.int32)
     got = _run(pc, wl.q, cu, 1)
-    whole = -(-pc.max_ctx // 16) * 16
+    whole = -(-pc.max_ctx // 64) * 64
     dec = pc.decode(partition=whole)
     assert torch.equal(got.view(torch.int32), dec.view(torch.int32))
     check_close(out_f64(got, "f32"), pc.ref_decode(), "f32")
+
+
+def test_prefill_one_row_fp32_matrix_cores():
+    """Config 2's shapes (fp32, head_dim 64: fp32 matrix cores): a one-row
+    chunk agrees with the oracle's decode and with pkv_decode."""
+    wl = make_workload(2, num_seqs=12)
+    pc = PoolCase(wl)
+    cu = np.arange(wl.num_seqs + 1, dtype=np.int32)
+    got = out_f64(_run(pc, wl.q, cu, 1), "f32")
+    ref = pc.ref_decode()
+    check_close(got, ref, "f32", "prefill")
+    check_close(got, out_f64(pc.decode(), "f32"), "f32", "vs decode")
 
 
 def test_prefill_one_row_matches_decode_matrix_cores():

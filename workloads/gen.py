@@ -113,6 +113,9 @@ class Workload:
     w_cu: np.ndarray              # int32 [W+1]
     seq_rows: list                # per sequence: int64 row index of each position 0..ctx-1
     prefix_tokens: int = 0
+    # shared-prefix groups: (first sequence, end sequence, shared tokens);
+    # one group of every sequence when prefix_tokens > 0
+    groups: list = field(default_factory=list)
     paired_write: bool = False
     prefill_chunk: int = 0
     _extra_gen: torch.Generator | None = field(default=None, repr=False)
@@ -217,30 +220,38 @@ def _fill_tables(ctx: np.ndarray, bs: int, maxb: int, order: np.ndarray,
 
 
 def _build(name, cfg_id, dtype, Hq, Hkv, hd, bs, NB, maxb, scale, ctx, tables,
-           prefix_tokens, g, paired_write=False, prefill_chunk=0) -> Workload:
+           prefix_tokens, g, paired_write=False, prefill_chunk=0, groups=None) -> Workload:
     S = len(ctx)
     ctx = np.asarray(ctx, dtype=np.int32)
-    # rows: the shared prefix first (once), then each sequence's own positions
+    if groups is None:
+        groups = [(0, S, prefix_tokens)] if prefix_tokens > 0 else []
+    opens = {s0: (s1, p) for (s0, s1, p) in groups}
+    # rows: each group's shared prefix (once), then its sequences' own positions
     seq_rows, w_first, w_counts, w_tabs = [], [], [], []
     n_rows = 0
-    if prefix_tokens > 0:
-        nbp = -(-prefix_tokens // bs)
-        t0 = np.zeros(maxb, dtype=np.int32)
-        t0[:nbp] = tables[0, :nbp]
-        for s in range(S):
-            assert np.array_equal(tables[s, :nbp], t0[:nbp]), "prefix blocks must be shared"
-        w_tabs.append(t0)
-        w_first.append(0)
-        w_counts.append(prefix_tokens)
-        n_rows = prefix_tokens
+    p, end, prow0 = 0, 0, 0
     for s in range(S):
+        if s in opens:
+            end, p = opens[s]
+            nbp = -(-p // bs)
+            t0 = np.zeros(maxb, dtype=np.int32)
+            t0[:nbp] = tables[s, :nbp]
+            for m in range(s, end):
+                assert np.array_equal(tables[m, :nbp], t0[:nbp]), "prefix blocks must be shared"
+            w_tabs.append(t0)
+            w_first.append(0)
+            w_counts.append(p)
+            prow0 = n_rows
+            n_rows += p
+        elif s >= end:
+            p = 0
         L = int(ctx[s])
-        own = max(0, L - prefix_tokens)
-        shared = min(L, prefix_tokens)
-        seq_rows.append(np.concatenate([np.arange(shared, dtype=np.int64),
+        own = max(0, L - p)
+        shared = min(L, p)
+        seq_rows.append(np.concatenate([prow0 + np.arange(shared, dtype=np.int64),
                                         n_rows + np.arange(own, dtype=np.int64)]))
         w_tabs.append(tables[s].copy())
-        w_first.append(prefix_tokens)
+        w_first.append(p)
         w_counts.append(own)
         n_rows += own
     w_cu = np.zeros(len(w_counts) + 1, dtype=np.int32)
@@ -255,7 +266,7 @@ def _build(name, cfg_id, dtype, Hq, Hkv, hd, bs, NB, maxb, scale, ctx, tables,
         block_tables=np.ascontiguousarray(tables, dtype=np.int32),
         k_rows=_to_storage(k, dtype), v_rows=_to_storage(v, dtype), q=_to_storage(q, dtype),
         w_tables=np.stack(w_tabs).astype(np.int32), w_first_pos=np.array(w_first, np.int32),
-        w_cu=w_cu, seq_rows=seq_rows, prefix_tokens=prefix_tokens,
+        w_cu=w_cu, seq_rows=seq_rows, prefix_tokens=prefix_tokens, groups=list(groups),
         paired_write=paired_write, prefill_chunk=prefill_chunk, _extra_gen=g)
 
 
@@ -305,3 +316,58 @@ def poison_pool(wl: Workload, bits: int | None = None) -> np.ndarray:
     if wl.dtype == F32:
         return np.full(wl.pool_shape, bits, dtype=np.uint32).view(np.float32)
     return np.full(wl.pool_shape, bits, dtype=np.uint16)
+
+
+def make_shared(group_sizes, prefix_tokens, tail=("uniform", 1, 64), *, dtype=BF16,
+                num_q_heads=8, num_kv_heads=1, head_dim=128, block_size=16,
+                short_members=0, num_blocks=None, seed=0, name="shared") -> Workload:
+    """Groups of consecutive sequences sharing a prompt: group i has
+    ``group_sizes[i]`` members whose tables start with the same
+    ``prefix_tokens[i] // block_size`` blocks (the prompt, written once); each
+    member adds its own tail of lengths drawn from ``tail`` (as ``ctx_dist``).
+    The first ``short_members`` members of each group instead stop inside the
+    prompt (context drawn from 1 .. prompt). Prompts are whole blocks. Draw
+    order: tails, short lengths, block permutation, K rows, V rows, q."""
+    assert len(group_sizes) == len(prefix_tokens)
+    assert all(p % block_size == 0 for p in prefix_tokens), "prompts are whole blocks"
+    g = torch.Generator().manual_seed(seed)
+    S = int(sum(group_sizes))
+    spec = ConfigSpec(0, name, dtype, S, num_q_heads, num_kv_heads, head_dim, block_size,
+                      1, 1, tail)
+    tails = _draw_ctx(spec, S, g).astype(np.int64)
+    shorts = torch.rand((S,), generator=g, dtype=torch.float64).numpy()
+    ctx = np.zeros(S, np.int64)
+    groups, s = [], 0
+    for n, p in zip(group_sizes, prefix_tokens):
+        for i in range(n):
+            if i < short_members and p > 0:
+                ctx[s + i] = 1 + int(shorts[s + i] * p) if p > 1 else 1
+            else:
+                ctx[s + i] = p + tails[s + i]
+        groups.append((s, s + n, int(p)))
+        s += n
+    need = sum(p // block_size for p in prefix_tokens) + sum(
+        max(0, -(-int(ctx[m]) // block_size) - prefix_tokens[gi] // block_size)
+        for gi, (s0, s1, _) in enumerate(groups) for m in range(s0, s1))
+    NB = int(num_blocks) if num_blocks is not None else need + 1
+    assert NB >= need + 1, "pool too small"
+    order = (torch.randperm(NB - 1, generator=g).numpy() + 1).astype(np.int32)
+    maxb = max([1] + [-(-int(c) // block_size) for c in ctx]
+               + [p // block_size for p in prefix_tokens])
+    tables = np.zeros((S, maxb), np.int32)
+    nxt = 0
+    for (s0, s1, p) in groups:
+        # every member's table starts with the whole prompt, also a short
+        # member's (which reads only the blocks its context reaches)
+        nbp = p // block_size
+        pre = order[nxt:nxt + nbp]
+        nxt += nbp
+        for m in range(s0, s1):
+            nb = -(-int(ctx[m]) // block_size)
+            tables[m, :nbp] = pre
+            own = max(0, nb - nbp)
+            tables[m, nbp:nbp + own] = order[nxt:nxt + own]
+            nxt += own
+    scale = 1.0 / math.sqrt(head_dim)
+    return _build(name, None, dtype, num_q_heads, num_kv_heads, head_dim, block_size, NB, maxb,
+                  scale, ctx.astype(np.int32), tables, 0, g, groups=groups)
