@@ -36,7 +36,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import paged_kv_cache_scatter_amd as pkv  # noqa: E402
-from workloads import CONFIGS, make_workload  # noqa: E402
+from workloads import CONFIGS, make_shared, make_workload  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 DEV = torch.device("cuda:0")
@@ -201,6 +201,100 @@ def time_decode_rotating(cfg: int, calls_per_set: int = 10):
             "seq_steps_per_s": round(wl.num_seqs / (ms * 1e-3), 1)}
 
 
+SHARED_WORKLOADS = {
+    # config 2: 30 sequences whose tables start with the same 32-token prompt
+    "config2": lambda: make_workload(2),
+    # 30 users of a ~500-token system prompt at the SmolLM2-135M shape: its 31
+    # full blocks (496 tokens) shared, own tails of 4 prompt tokens + 8..200
+    "smollm2-500": lambda: make_shared([30], [496], ("uniform", 12, 204), dtype="f32",
+                                       num_q_heads=9, num_kv_heads=3, head_dim=64, seed=21,
+                                       name="smollm2-135m-fp32-500-token-shared-prompt"),
+    # 64 sequences of the LLaMA-2-70B layer shape sharing a 4096-token prompt,
+    # own tails of 1..4096 tokens
+    "llama70b-4096": lambda: make_shared([64], [4096], ("uniform", 1, 4096), dtype="bf16",
+                                         num_q_heads=64, num_kv_heads=8, head_dim=128, seed=23,
+                                         name="llama-2-70b-layer-bf16-4096-token-shared-prompt"),
+}
+
+
+def time_shared(name: str, calls_per_set: int = 20, partition: int = 0):
+    """pkv_decode_shared against pkv_decode on the same inputs. Small workloads
+    are replicated over disjoint block sets of one pool (same values), cycled
+    so that consecutive calls do not hit the Infinity Cache."""
+    wl = SHARED_WORKLOADS[name]()
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    row_b = wl.num_kv_heads * wl.head_dim * wl.itemsize * 2          # K + V of one token
+    used = int(wl.w_cu[-1]) * row_b
+    sets = int(max(1, min(24, -(-(512 << 20) // max(used, 1)))))
+    nb1 = wl.num_blocks - 1
+    pool = (1 + sets * nb1, wl.block_size, wl.num_kv_heads, wl.head_dim)
+    k_pool = torch.zeros(pool, dtype=dt, device=DEV)
+    v_pool = torch.zeros(pool, dtype=dt, device=DEV)
+    shift = lambda t, r: np.where(t > 0, t + r * nb1, 0).astype(np.int32)
+    kr, vr = to_dev(wl.k_rows), to_dev(wl.v_rows)
+    n = int(wl.w_cu[-1])
+    tables = []
+    for r in range(sets):
+        slots = pkv.slot_mapping(to_dev(shift(wl.w_tables, r)), to_dev(wl.w_first_pos),
+                                 to_dev(wl.w_cu), n, wl.block_size, pool[0])
+        pkv.write(kr, vr, slots, k_pool, v_pool)
+        tables.append(to_dev(shift(wl.block_tables, r)))
+    q, ctx = to_dev(wl.q), to_dev(wl.context_lens)
+    max_ctx = int(wl.context_lens.max())
+    gs = np.array([g[0] for g in wl.groups] + [wl.num_seqs], np.int32)
+    pl = np.array([g[2] for g in wl.groups], np.int32)
+    sizes = np.diff(gs)
+    tails = [int(wl.context_lens[s]) - min(int(wl.context_lens[s]), int(pl[i]))
+             for i in range(len(pl)) for s in range(gs[i], gs[i + 1])]
+    max_tail = max(tails)
+    out = torch.empty_like(q)
+    G, mg, mp = len(pl), int(sizes.max()), int(pl.max())
+    ws_s = torch.empty(max(16, pkv.decode_shared_workspace_bytes(
+        wl.num_seqs, wl.num_q_heads, max_ctx, G, mg, mp, max_tail, k_pool, partition)),
+        dtype=torch.uint8, device=DEV)
+    part = pkv.decode_partition(wl.num_seqs, max_ctx, k_pool)
+    ws_p = torch.empty(max(16, pkv.decode_workspace_bytes(wl.num_seqs, wl.num_q_heads, max_ctx,
+                                                          k_pool, part)),
+                       dtype=torch.uint8, device=DEV)
+    gs_d, pl_d = to_dev(gs), to_dev(pl)
+
+    def shared(tb):
+        pkv.decode_shared(q, k_pool, v_pool, tb, ctx, gs_d, pl_d, wl.scale, max_ctx, mg, mp,
+                          max_tail_len=max_tail, out=out, partition=partition, workspace=ws_s)
+
+    def plain(tb):
+        pkv.decode(q, k_pool, v_pool, tb, ctx, wl.scale, max_ctx, out=out, partition=part,
+                   workspace=ws_p)
+
+    def timed(fn):
+        for r in range(2 * sets):
+            fn(tables[r % sets])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        calls = sets * calls_per_set
+        e0.record()
+        for r in range(calls):
+            fn(tables[r % sets])
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / calls
+
+    ms_plain = timed(plain)
+    ms_shared = timed(shared)
+    kv_plain = wl.kv_bytes_per_call()                 # every sequence reads its whole context
+    kv_unique = (int(pl.sum()) + sum(tails)) * row_b  # each prompt once, each tail once
+    return {"workload": f"{wl.name}: {len(pl)} group(s) of {mg} max, prompt {mp} tokens, "
+                        f"{wl.num_seqs} seqs, {wl.num_q_heads} q / {wl.num_kv_heads} kv heads, "
+                        f"head_dim {wl.head_dim}, block {wl.block_size}, {wl.dtype}",
+            "rotating_sets": sets, "total_context_tokens": wl.total_ctx,
+            "plain_us": round(ms_plain * 1e3, 2), "shared_us": round(ms_shared * 1e3, 2),
+            "speedup": round(ms_plain / ms_shared, 3),
+            "plain_kv_bytes": kv_plain, "shared_unique_kv_bytes": kv_unique,
+            "plain_GBps": round(kv_plain / (ms_plain * 1e-3) / 1e9, 1),
+            "shared_unique_GBps": round(kv_unique / (ms_shared * 1e-3) / 1e9, 1),
+            "shared_context_tokens_per_s": round(wl.total_ctx / (ms_shared * 1e-3), 1)}
+
+
 def cpu_baseline(wl, budget_s: float = 12.0, max_passes: int = 20):
     """The fp64 oracle on the host, over the sequences of the same workload, in
     order and in repeated passes, until ``budget_s`` of CPU time is spent. Each
@@ -327,7 +421,16 @@ def main():
     ap.add_argument("--summarize-counters", nargs=4, metavar="DIR",
                     help="FETCH_SIZE and WRITE_SIZE run directories of the decode kernel, "
                          "then of the copy calibration: write the traffic file")
+    ap.add_argument("--shared", nargs="+", choices=sorted(SHARED_WORKLOADS), metavar="WL",
+                    help="only time the shared-prefix decode against plain decode on these "
+                         f"workloads ({', '.join(sorted(SHARED_WORKLOADS))})")
     args = ap.parse_args()
+    if args.shared:
+        pkv.load()
+        for name in args.shared:
+            print(f"[bench] shared-prefix decode, {name}", file=sys.stderr, flush=True)
+            print(json.dumps({"shared_prefix_decode": time_shared(name)}), flush=True)
+        return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters, copy_bytes=512 << 20)
         return
