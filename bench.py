@@ -295,6 +295,50 @@ def time_shared(name: str, calls_per_set: int = 20, partition: int = 0):
             "shared_context_tokens_per_s": round(wl.total_ctx / (ms_shared * 1e-3), 1)}
 
 
+def time_layer_graph(cfg: int, layers: int = 16, steps: int = 20):
+    """A decode step over ``layers`` layers (fused write + decode + merge per
+    layer, one layered pool, one table), launched layer by layer against the
+    same step replayed from one captured HIP graph. Pool values are N(0,1)
+    drawn on the device (the timing does not depend on them)."""
+    from paged_kv_cache_scatter_amd.graph import LayerSteps
+    wl = make_workload(cfg)
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    L, S = layers, wl.num_seqs
+    g = torch.Generator(device=DEV).manual_seed(cfg)
+    kp = torch.empty((L,) + wl.pool_shape, dtype=dt, device=DEV)
+    vp = torch.empty_like(kp)
+    for x in (kp, vp):
+        for layer in range(L):
+            x[layer].normal_(generator=g)
+    q = torch.randn((L, S, wl.num_q_heads, wl.head_dim), generator=g, device=DEV).to(dt)
+    kn = torch.randn((L, S, wl.num_kv_heads, wl.head_dim), generator=g, device=DEV).to(dt)
+    vn = torch.randn((L, S, wl.num_kv_heads, wl.head_dim), generator=g, device=DEV).to(dt)
+    st = LayerSteps(q, kn, vn, kp, vp, to_dev(wl.block_tables), to_dev(wl.context_lens),
+                    wl.scale, int(wl.context_lens.max()))
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms_eager = timed(st.run)
+    st.capture()
+    ms_graph = timed(st.replay)
+    kvb = wl.kv_bytes_per_call() * L
+    return {"workload": workload_label(wl) + f", {L} layers", "partition": st.partition,
+            "launches_per_step": 2 * L, "eager_us": round(ms_eager * 1e3, 2),
+            "graph_us": round(ms_graph * 1e3, 2), "speedup": round(ms_eager / ms_graph, 3),
+            "graph_us_per_layer": round(ms_graph * 1e3 / L, 2),
+            "kv_bytes_per_step": kvb, "graph_GBps": round(kvb / (ms_graph * 1e-3) / 1e9, 1)}
+
+
 def cpu_baseline(wl, budget_s: float = 12.0, max_passes: int = 20):
     """The fp64 oracle on the host, over the sequences of the same workload, in
     order and in repeated passes, until ``budget_s`` of CPU time is spent. Each
@@ -424,7 +468,17 @@ def main():
     ap.add_argument("--shared", nargs="+", choices=sorted(SHARED_WORKLOADS), metavar="WL",
                     help="only time the shared-prefix decode against plain decode on these "
                          f"workloads ({', '.join(sorted(SHARED_WORKLOADS))})")
+    ap.add_argument("--layer-graph", nargs="+", type=int, metavar="CFG",
+                    help="only time a 16-layer decode step of these configs, layer by layer "
+                         "and replayed from one captured HIP graph")
     args = ap.parse_args()
+    if args.layer_graph:
+        pkv.load()
+        for cfg in args.layer_graph:
+            print(f"[bench] 16-layer step, config {cfg}", file=sys.stderr, flush=True)
+            print(json.dumps({"layer_step_graph": time_layer_graph(cfg)}), flush=True)
+            torch.cuda.empty_cache()
+        return
     if args.shared:
         pkv.load()
         for name in args.shared:

@@ -6,6 +6,6 @@ method's arithmetic: no slot computation, no gather, no attention. Both the
 oracle (``oracle/``) and the HIP path consume what it returns.
 """
 
-from .gen import (CONFIGS, Workload, kv_bytes, make_custom, make_shared,  # noqa: F401
-                  make_workload, poison_pool)  # noqa: F401
+from .gen import (CONFIGS, Workload, kv_bytes, make_custom, make_layers,  # noqa: F401
+                  make_shared, make_workload, poison_pool)
 from .engine import TokenRows, engine_requests  # noqa: F401

@@ -22,7 +22,7 @@ numbers and lays out which token rows a write covers.
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 
 import numpy as np
 import torch
@@ -371,3 +371,20 @@ def make_shared(group_sizes, prefix_tokens, tail=("uniform", 1, 64), *, dtype=BF
     scale = 1.0 / math.sqrt(head_dim)
     return _build(name, None, dtype, num_q_heads, num_kv_heads, head_dim, block_size, NB, maxb,
                   scale, ctx.astype(np.int32), tables, 0, g, groups=groups)
+
+
+def make_layers(wl: Workload, num_layers: int, seed: int = 0) -> list:
+    """``num_layers`` workloads sharing ``wl``'s tables, lengths and write
+    segments (one table serves every layer), each with its own K/V rows and
+    queries drawn N(0,1) from ``manual_seed(seed * 1000 + layer)`` (K, V, q)."""
+    out = []
+    for layer in range(num_layers):
+        g = torch.Generator().manual_seed(seed * 1000 + layer)
+        shp = wl.k_rows.shape
+        k = torch.randn(shp, generator=g)
+        v = torch.randn(shp, generator=g)
+        q = torch.randn(wl.q.shape, generator=g)
+        out.append(replace(wl, name=f"{wl.name}[layer {layer}]", k_rows=_to_storage(k, wl.dtype),
+                           v_rows=_to_storage(v, wl.dtype), q=_to_storage(q, wl.dtype),
+                           _extra_gen=None, _prefill_q=None))
+    return out
