@@ -227,13 +227,25 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // Direct-to-LDS staging: global_load_lds_dwordx4 writes lane i's 16 bytes
 // at LDS address M0 + 16*i, without passing through registers. The compiler
 // does not see these writes, so the waits on them are explicit.
+// NT: non-temporal hint, for rows read once in a stream larger than the
+// caches (the decode's K/V rows).
+template <bool NT = false>
 __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(gaddr), "s"(lds) : "memory");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :: "v"(gaddr), "s"(lds) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(gaddr), "s"(lds) : "memory");
 }
+template <bool NT = false>
 __device__ __forceinline__ void dma16s(const char* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(sbase), "s"(lds) : "memory");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :: "v"(voff), "s"(sbase), "s"(lds) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(sbase), "s"(lds) : "memory");
 }
 // The same for one 4-byte word per lane (lane i -> M0 + 4*i).
 __device__ __forceinline__ void dma4(const void* gaddr, uint32_t lds) {
