@@ -130,13 +130,21 @@ pkv_status pkv_write(const void* k, const void* v, const int32_t* slot_mapping,
  * (v_pool), KV head h / (num_q_heads / num_kv_heads). Accumulation is fp32;
  * a bf16 result is rounded to nearest even.
  *
- * Sequences are cut into splits of `partition` tokens (a multiple of the
- * block size; 0 picks one from the sizes, see pkv_decode_partition). Each
- * split yields a partial (running max m in log2 units, exp-sum l, unnormalised
- * o) in `workspace`; a second kernel merges the partials of sequences that
- * have more than one split. Sequences with a single split are written
- * directly. workspace (device) must hold pkv_decode_workspace_bytes(...)
- * bytes; it may be NULL when that is 0. Its contents need no initialisation.
+ * Sequences are cut into pieces of `partition` tokens (a multiple of the
+ * block size; 0 picks one from the sizes, see pkv_decode_partition). With at
+ * most 1024 sequences each context is cut into full pieces of `partition`
+ * tokens, then full pieces of half that, then its rest, and the launch runs
+ * all large pieces first, then the small ones, then the rests (equal pieces
+ * keep every workgroup stream of the GPU equally loaded and the last pieces
+ * short). Each piece of a sequence with more than one yields a partial
+ * (running max m in log2 units, exp-sum l, unnormalised o) in `workspace`;
+ * the last workgroup of a (sequence, KV head) to finish merges them in the
+ * same launch, counted by one int32 per (sequence, KV head) at the end of
+ * the workspace. Sequences with a single piece are written directly.
+ * workspace (device) must hold pkv_decode_workspace_bytes(...) bytes; it may
+ * be NULL when that is 0. Its counter words must be zero before the first
+ * call that uses it (a zero-filled buffer); every call leaves them zero.
+ * Calls that share a workspace must not overlap (run them in stream order).
  *
  * context_lens[s] is clamped to [0, min(max_context_len,
  * max_blocks_per_seq * block_size)]; a sequence of length 0 gets zeros.
@@ -165,7 +173,10 @@ pkv_status pkv_decode(const void* q, int32_t num_seqs, int32_t num_q_heads,
                       void* stream);
 
 /* The two phases of pkv_decode, for callers that time or schedule them
- * separately. Call both, in this order, with identical arguments. */
+ * separately: every piece's partial, then a second kernel that merges them.
+ * Call both, in this order, with identical arguments. They leave the counter
+ * words of the workspace untouched, and their result is bit-identical to
+ * pkv_decode's. */
 pkv_status pkv_decode_partials(const void* q, int32_t num_seqs, int32_t num_q_heads,
                                const void* k_pool, const void* v_pool,
                                const pkv_pool_desc* pool,
@@ -201,8 +212,11 @@ pkv_status pkv_decode_reduce(const void* q, int32_t num_seqs, int32_t num_q_head
  * across sequences (as for pkv_write). Other arguments, the workspace and the
  * errors are those of pkv_decode; k_new and v_new must be 16-byte aligned.
  *
- * pkv_decode_step_partials is its first phase (the fused write and the split
- * partials); pkv_decode_reduce with the same arguments completes it.
+ * One launch: the fused write, every piece, and the merge of the pieces in
+ * the same launch (workspace counters as for pkv_decode).
+ * pkv_decode_step_partials is its first phase (the fused write and the
+ * partials, counters untouched); pkv_decode_reduce with the same arguments
+ * completes it.
  * ------------------------------------------------------------------------- */
 pkv_status pkv_decode_step(const void* q, const void* k_new, const void* v_new,
                            int32_t num_seqs, int32_t num_q_heads, void* k_pool,
@@ -253,7 +267,10 @@ pkv_status pkv_decode_step_partials(const void* q, const void* k_new, const void
  *   are not attended). partition: tokens per tail split (0 = auto from
  *   max_tail_len), as in pkv_decode.
  * workspace: pkv_decode_shared_workspace_bytes(...) bytes (device, 16-byte
- *   aligned); 0 when no shared pass and no split is needed.
+ *   aligned); 0 when no shared pass and no split is needed. Its counter words
+ *   (at the end) must be zero before the first call, as for pkv_decode; the
+ *   tail launch merges the shared and tail partials, so a call is two launches
+ *   (shared pass, tails + merge).
  * With num_groups == 0, max_prefix_len < block_size, or a shape the shared
  * pass does not compile (it covers bf16 and fp32 pools, head_dim 64 and 128,
  * group size 1..8), the call is exactly pkv_decode. Errors are those of

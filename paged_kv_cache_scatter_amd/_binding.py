@@ -223,7 +223,7 @@ def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     _dev(out, "out", q.dtype, q.shape)
     need = decode_workspace_bytes(S, Hq, max_context_len, k_pool, partition)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0
     if workspace is not None:
         _dev(workspace, "workspace", torch.uint8)
@@ -278,7 +278,7 @@ def decode_shared(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     need = decode_shared_workspace_bytes(S, Hq, max_context_len, G, max_group_size,
                                          max_prefix_len, max_tail_len, k_pool, partition)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0
     if workspace is not None:
         _dev(workspace, "workspace", torch.uint8)
@@ -316,7 +316,7 @@ def decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
     _dev(out, "out", q.dtype, q.shape)
     need = decode_workspace_bytes(S, Hq, max_context_len, k_pool, partition)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0
     if workspace is not None:
         _dev(workspace, "workspace", torch.uint8)

@@ -57,10 +57,24 @@ pkv_status check_pool(const pkv_pool_desc* pool) {
 struct DecodePlan {
   int rep = 0;
   int partition = 0;
-  int splits = 0;
+  int splits = 0;       // partial slots per (sequence, head)
+  int sched_q = 0;      // small piece of the piece schedule (0: plain split grid)
   size_t ws_ml_bytes = 0;
+  size_t ws_cnt_offset = 0;   // merge counters [S, Hkv] int32, after the partials
   size_t ws_bytes = 0;
 };
+
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Partials [S, Hq, J] (m, l) and o, then the merge counters.
+void plan_workspace(int32_t num_seqs, int32_t num_q_heads, const pkv_pool_desc* pool, int J,
+                    DecodePlan* plan) {
+  const size_t rows = (size_t)num_seqs * num_q_heads * J;
+  plan->ws_ml_bytes = round256(rows * 2 * sizeof(float));
+  plan->ws_cnt_offset = round256(plan->ws_ml_bytes + rows * (size_t)pool->head_dim * sizeof(float));
+  plan->ws_bytes = plan->ws_cnt_offset +
+                   round256((size_t)num_seqs * pool->num_kv_heads * sizeof(int32_t));
+}
 
 int align_tokens(const pkv_pool_desc* pool) {
   const int tile = decode_tile_tokens(pool->head_dim * dtype_bytes(pool->dtype));
@@ -74,14 +88,16 @@ int auto_partition(int num_seqs, int max_ctx, const pkv_pool_desc* pool) {
   if (max_ctx <= 0 || num_seqs <= 0) return align;
   // With at least four (sequence, KV head) units per CU there is enough
   // parallelism without splitting. Otherwise split so that, with lengths
-  // spread up to max_ctx, there are about 16 split workgroups per CU
-  // (measured on the LLaMA-2-70B-layer workload: 512-token splits).
+  // spread up to max_ctx, there are about 8 split workgroups per CU. Each
+  // split workgroup costs a prologue and, with the merge in the launch, a
+  // counted partial; measured on the LLaMA-2-70B-layer workload: 1024-token
+  // splits 150 us, 512-token 172 us, 2048-token 164 us.
   const double units = (double)num_seqs * pool->num_kv_heads;
   int part;
   if (units >= 4.0 * kNumCUs) {
     part = whole;
   } else {
-    const double p = units * (double)max_ctx / (32.0 * kNumCUs);
+    const double p = units * (double)max_ctx / (16.0 * kNumCUs);
     part = 256;
     while (part < p && part < cap) part <<= 1;
   }
@@ -94,7 +110,7 @@ int auto_partition(int num_seqs, int max_ctx, const pkv_pool_desc* pool) {
 
 pkv_status plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
                        int32_t max_ctx, int32_t partition, const pkv_pool_desc* pool,
-                       DecodePlan* plan) {
+                       DecodePlan* plan, bool allow_sched = true) {
   pkv_status st = check_pool(pool);
   if (st != PKV_OK) return st;
   if (num_seqs < 0 || num_q_heads < 1 || max_ctx < 0 || max_blocks < 1) {
@@ -136,11 +152,21 @@ pkv_status plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks
   plan->rep = rep;
   plan->partition = part;
   plan->splits = splits;
-  if (splits > 1) {
-    const size_t rows = (size_t)num_seqs * num_q_heads * splits;
-    plan->ws_ml_bytes = ((rows * 2 * sizeof(float)) + 255) & ~(size_t)255;
-    plan->ws_bytes = plan->ws_ml_bytes + rows * (size_t)pool->head_dim * sizeof(float);
+  plan->sched_q = 0;
+  if (splits > 1 && allow_sched && num_seqs <= kSchedMaxSeqs) {
+    // piece schedule: full pieces of `part` tokens, then of half of it
+    // (rounded to the alignment), then each sequence's rest. Measured on the
+    // LLaMA-2-70B-layer workload (1024-token pieces): halves 140 us,
+    // quarters 141 us, eighths 150 us; no small pieces 149 us.
+    const int q = std::max(align, (part / 2) / align * align);
+    const int64_t J = (int64_t)max_ctx / part + (part - 1) / q + 1;
+    if (J <= kMaxSplits) {
+      plan->sched_q = q;
+      plan->splits = (int)J;
+    }
   }
+  plan->ws_ml_bytes = plan->ws_cnt_offset = plan->ws_bytes = 0;
+  if (plan->splits > 1) plan_workspace(num_seqs, num_q_heads, pool, plan->splits, plan);
   return PKV_OK;
 }
 
@@ -177,7 +203,7 @@ pkv_status plan_shared(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks
       !shared_pass_supported(pool->dtype, pool->head_dim, plan->rep))
     return PKV_OK;
   const int tail = in.max_tail < 0 ? max_ctx : in.max_tail;
-  st = plan_decode(num_seqs, num_q_heads, max_blocks, tail, partition, pool, plan);
+  st = plan_decode(num_seqs, num_q_heads, max_blocks, tail, partition, pool, plan, false);
   if (st != PKV_OK) return st;
   const int64_t align = std::max(kSharedAlign, bs);
   const int64_t row_tiles = ((int64_t)in.max_group * plan->rep + kSharedRows - 1) / kSharedRows;
@@ -194,9 +220,7 @@ pkv_status plan_shared(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks
     return PKV_ERR_UNSUPPORTED;
   }
   plan->splits = (int)J;
-  const size_t rows = (size_t)num_seqs * num_q_heads * J;
-  plan->ws_ml_bytes = ((rows * 2 * sizeof(float)) + 255) & ~(size_t)255;
-  plan->ws_bytes = plan->ws_ml_bytes + rows * (size_t)pool->head_dim * sizeof(float);
+  plan_workspace(num_seqs, num_q_heads, pool, (int)J, plan);
   sd->group_start = in.group_start;
   sd->prefix_lens = in.prefix_lens;
   sd->num_groups = in.num_groups;
@@ -274,12 +298,17 @@ pkv_status decode_impl(Phase phase, const void* q, int32_t num_seqs, int32_t num
   a.max_ctx = max_ctx;
   a.partition = plan.partition;
   a.num_splits = plan.splits;
+  a.sched_q = plan.sched_q;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.cu_q = nullptr;
   a.total_q = 0;
   a.k_new = k_new;
   a.v_new = v_new;
   a.sh = sd;
+  // One launch merges its own partials unless the caller runs the phases apart.
+  a.counters = (phase == Phase::kBoth && plan.ws_bytes)
+                   ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.ws_cnt_offset)
+                   : nullptr;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (sd.group_start && phase != Phase::kReduce) {
     PrefillArgs p{};
@@ -309,7 +338,7 @@ pkv_status decode_impl(Phase phase, const void* q, int32_t num_seqs, int32_t num
     st = launch_decode_partials(a, pool->dtype, pool->head_dim, plan.rep, s);
     if (st != PKV_OK) return st;
   }
-  if (phase != Phase::kPartials) {
+  if (phase == Phase::kReduce) {
     st = launch_decode_reduce(a, pool->dtype, pool->head_dim, s);
     if (st != PKV_OK) return st;
   }

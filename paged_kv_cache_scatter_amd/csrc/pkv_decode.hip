@@ -206,6 +206,14 @@ __device__ __forceinline__ int head_base(int kc) {
   }
 }
 
+// The value of lane + W (W <= 8: a DPP row shift, lane i reads lane i + W of
+// its 16-lane row, which holds the next token for lanes of even tokens).
+template <int W>
+__device__ __forceinline__ float next_token(float x) {
+  if constexpr (W <= 8) return dpp<0x100 + W>(x);   // row_shl:W
+  else return __shfl_xor(x, W);
+}
+
 // Max / sum over lanes congruent modulo STRIDE (power of two), result in every lane.
 template <int STRIDE, bool MAX>
 __device__ __forceinline__ float strided_reduce(float x) {
@@ -214,8 +222,8 @@ __device__ __forceinline__ float strided_reduce(float x) {
   if constexpr (STRIDE <= 2) x = op(x, dpp<kRowRor + 2>(x));
   if constexpr (STRIDE <= 4) x = op(x, dpp<kRowRor + 4>(x));
   if constexpr (STRIDE <= 8) x = op(x, dpp<kRowRor + 8>(x));
-  if constexpr (STRIDE <= 16) x = op(x, swz_xor16(x));
-  if constexpr (STRIDE <= 32) x = op(x, xor32(x));
+  if constexpr (STRIDE <= 16) x = join16<MAX>(x);
+  if constexpr (STRIDE <= 32) x = join32<MAX>(x);
   return x;
 }
 
@@ -374,7 +382,7 @@ __device__ __forceinline__ bool tile_softmax(
       ps += p;
       const int tt = r * G::TPW_K + kg;
       if constexpr (G::ISZ == 2) {
-        const float pn = __shfl_xor(p, G::LPT_K);   // same head, token tt ^ 1
+        const float pn = next_token<G::LPT_K>(p);   // same head, token tt + 1
         if (dup0 && h < REP && !(kg & 1)) pbuf[(tt >> 1) * G::PSTR + h] = pack_bf16x2(p, pn);
       } else {
         if (dup0 && h < REP) reinterpret_cast<float*>(pbuf)[tt * G::PSTR + h] = p;
@@ -665,6 +673,222 @@ struct Lds {
   }
 };
 
+// Device-coherent (agent-scope) store and load of one float: the store is
+// written through the XCD's L2, the load is not served from a stale L2 line.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Merge of one (sequence, KV head)'s split partials into the output rows of
+// its REP query heads: M = max m_i, L = sum l_i 2^(m_i - M), out = sum
+// 2^(m_i - M) o_i / L. Slots 0 .. nps-1 hold the shared pass's partials, the
+// decode splits follow from slot0. Head h is merged by wave h % kWaves; lane
+// l owns dims l, l + 64, ... Lane i reads slot i's (m, l) with one 8-byte
+// load; the o rows of kMergeBatch slots are loaded together before they are
+// summed, in slot order (the same order, hence the same bits, as the merge
+// kernel). wl is the wave's 64-float LDS scratch (more than 64 partials).
+constexpr int kMergeBatch = 8;
+
+__device__ __forceinline__ float2 ld_agent2(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+
+template <typename T, int HD, int REP>
+__device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int hq0, int nps,
+                                               int slot0, int nsplit, T* out, float* wl, int w,
+                                               int lane) {
+  constexpr int DPT = HD >= 64 ? HD / 64 : 1;   // dims per lane
+  const int n = nps + nsplit;
+  const int J = a.num_splits;
+  auto slot = [&](int i) { return i < nps ? i : slot0 + i - nps; };
+  for (int h = w; h < REP; h += kWaves) {
+    const size_t row0 = ((size_t)s * a.num_q_heads + hq0 + h) * J;
+    const float* ml = a.ws_ml + row0 * 2;
+    const float* po = a.ws_o + row0 * HD;
+    float M = -INFINITY, Ls = 0.f, f = 0.f;
+    if (n <= 64) {
+      const float2 v = lane < n ? ld_agent2(ml + 2 * slot(lane)) : make_float2(-INFINITY, 0.f);
+      M = group_max<64>(v.x);
+      if (lane < n && M != -INFINITY) {
+        f = fast_exp2(v.x - M);
+        Ls = fmaf(v.y, f, 0.f);
+      }
+    } else {
+      for (int i = lane; i < n; i += 64) M = fmaxf(M, ld_agent(ml + 2 * slot(i)));
+      M = group_max<64>(M);
+    }
+    float acc[DPT];
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) acc[e] = 0.f;
+    for (int c = 0; c < n; c += 64) {
+      if (n > 64) {
+        const int i = c + lane;
+        f = 0.f;
+        if (i < n && M != -INFINITY) {
+          f = fast_exp2(ld_agent(ml + 2 * slot(i)) - M);
+          Ls = fmaf(ld_agent(ml + 2 * slot(i) + 1), f, Ls);
+        }
+      }
+      wl[lane] = f;   // read back by the same wave: LDS keeps a wave's order
+      const int m = min(64, n - c);
+      for (int k0 = 0; k0 < m; k0 += kMergeBatch) {
+        float ov[kMergeBatch][DPT];
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k) {
+          const float* pk = po + (size_t)slot(c + min(k0 + k, m - 1)) * HD;
+#pragma unroll
+          for (int e = 0; e < DPT; ++e) {
+            const int d = lane + 64 * e;
+            ov[k][e] = d < HD ? ld_agent(pk + d) : 0.f;
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k) {
+          if (k0 + k < m) {
+            const float fk = wl[k0 + k];
+#pragma unroll
+            for (int e = 0; e < DPT; ++e) acc[e] = fmaf(fk, ov[k][e], acc[e]);
+          }
+        }
+      }
+    }
+    Ls = group_sum<64>(Ls);
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) {
+      const int d = lane + 64 * e;
+      if (d < HD) out[h * HD + d] = from_f32<T>(Ls > 0.f ? acc[e] / Ls : 0.f);
+    }
+  }
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts, then
+// the row broadcasts of lanes 15 and 31).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xF, true);
+}
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += dpp_u<0x111>(x);         // row_shr:1
+  x += dpp_u<0x112>(x);         // row_shr:2
+  x += dpp_u<0x114>(x);         // row_shr:4
+  x += dpp_u<0x118>(x);         // row_shr:8
+  x += dpp_u<0x142, 0xA>(x);    // row_bcast:15 into rows 1 and 3
+  x += dpp_u<0x143, 0xC>(x);    // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
+// A workgroup's piece under the piece schedule.
+struct Piece {
+  int s, t0, t1, slot, n, ctx;
+};
+
+// Piece number `pid` of the schedule (see DecodeArgs::sched_q): every thread
+// counts the pieces of four consecutive sequences, a workgroup scan gives
+// each thread its offsets in the three segments (full large pieces, full
+// small pieces, rests), and the thread holding the piece publishes it.
+// Returns false (uniformly) when pid is past the last piece. `lds` holds at
+// least 32 ints; the caller synchronises before reusing it.
+__device__ __forceinline__ bool find_piece(const DecodeArgs& a, int pid, int lim, Piece& pc,
+                                        int* lds) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int P = a.partition, Q = a.sched_q;
+  int L[4];
+  PieceCounts pcs[4];
+  uint32_t nbig = 0, nsr = 0;   // large pieces; (small << 16) | rests
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int sq = tid * 4 + i;
+    int c = sq < a.num_seqs ? a.ctx_lens[sq] : 0;
+    c = c < 0 ? 0 : (c > lim ? lim : c);
+    L[i] = c;
+    pcs[i] = sq < a.num_seqs ? piece_counts(c, P, Q) : PieceCounts{0, 0, 0};
+    nbig += pcs[i].big;
+    nsr += ((uint32_t)pcs[i].small << 16) | (uint32_t)pcs[i].rest;
+  }
+  const uint32_t ib = wave_incl_scan(nbig), is = wave_incl_scan(nsr);
+  if (lane == 63) {
+    lds[w] = (int)ib;
+    lds[4 + w] = (int)is;
+  }
+  lds[16] = -1;
+  __syncthreads();
+  uint32_t pb = 0, ps = 0, tb = 0, ts = 0;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) {
+    const uint32_t vb = (uint32_t)lds[k], vs = (uint32_t)lds[4 + k];
+    if (k < w) {
+      pb += vb;
+      ps += vs;
+    }
+    tb += vb;
+    ts += vs;
+  }
+  const uint32_t eb = pb + ib - nbig;   // large pieces before this thread's
+  const uint32_t es = ps + is - nsr;
+  const uint32_t tsmall = ts >> 16, trest = ts & 0xFFFF;
+  const uint32_t u = (uint32_t)pid;
+  // segment of pid and its index within the segment
+  int seg;
+  uint32_t k;
+  if (u < tb) {
+    seg = 0;
+    k = u - eb;
+  } else if (u < tb + tsmall) {
+    seg = 1;
+    k = u - tb - (es >> 16);
+  } else if (u < tb + tsmall + trest) {
+    seg = 2;
+    k = u - tb - tsmall - (es & 0xFFFF);
+  } else {
+    return false;
+  }
+  const uint32_t mine = seg == 0 ? nbig : seg == 1 ? (nsr >> 16) : (nsr & 0xFFFF);
+  if (k < mine) {   // this thread holds the piece (unsigned: k < 0 wraps)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t ni = seg == 0 ? pcs[i].big : seg == 1 ? pcs[i].small : pcs[i].rest;
+      if (k < ni) {
+        const PieceCounts& c = pcs[i];
+        int t0, t1, slot;
+        if (seg == 0) {
+          t0 = (int)k * P;
+          t1 = t0 + P;
+          slot = (int)k;
+        } else if (seg == 1) {
+          t0 = c.big * P + (int)k * Q;
+          t1 = t0 + Q;
+          slot = c.big + (int)k;
+        } else {
+          t0 = c.big * P + c.small * Q;
+          t1 = L[i];
+          slot = c.big + c.small;
+        }
+        lds[16] = tid * 4 + i;
+        lds[17] = t0;
+        lds[18] = t1;
+        lds[19] = slot;
+        lds[20] = c.big + c.small + c.rest;
+        lds[21] = L[i];
+        break;
+      }
+      k -= ni;
+    }
+  }
+  __syncthreads();
+  pc.s = lds[16];
+  pc.t0 = lds[17];
+  pc.t1 = lds[18];
+  pc.slot = lds[19];
+  pc.n = lds[20];
+  pc.ctx = lds[21];
+  return pc.s >= 0;
+}
+
 template <typename T, int HD, int REP>
 __global__ void __launch_bounds__(kThreads)
 decode_partials_kernel(DecodeArgs a) {
@@ -683,7 +907,23 @@ decode_partials_kernel(DecodeArgs a) {
   const int lim = min(a.max_ctx, a.max_blocks << bshift);
   int qrow = s;   // row of q and out
   int ctx;
-  if (a.cu_q) {
+  // piece schedule: this workgroup's sequence, token range and partial slot
+  Piece pc{};
+  const bool sched = a.sched_q > 0;
+  if (sched) {
+    if (!find_piece(a, blockIdx.y + gridDim.y * blockIdx.z, lim, pc,
+                    reinterpret_cast<int*>(smem)))
+      return;
+    // memory safety whatever the scan gave: an inconsistent piece does no work
+    if ((unsigned)pc.s >= (unsigned)a.num_seqs || pc.t0 < 0 || pc.t0 > pc.t1 ||
+        pc.t1 > pc.ctx || pc.ctx > lim || (unsigned)pc.slot >= (unsigned)a.num_splits ||
+        pc.n > a.num_splits)
+      return;
+    __syncthreads();   // the scan's LDS words are reused below
+    s = qrow = pc.s;
+    j = pc.slot;
+    ctx = pc.ctx;
+  } else if (a.cu_q) {
     // prefill row: its own causal context, one split
     qrow = blockIdx.y * gridDim.z + blockIdx.z;
     j = 0;
@@ -709,7 +949,9 @@ decode_partials_kernel(DecodeArgs a) {
   int start = 0, nps = 0, slot0 = 0;
   const int P = a.partition;
   int nsplit;
-  if (a.sh.group_start) {
+  if (sched) {
+    nsplit = pc.n;
+  } else if (a.sh.group_start) {
     start = min(ctx, shared_len(a.sh, group_of(a.sh, s), lim, bshift));
     nps = (start + a.sh.prefix_part - 1) / a.sh.prefix_part;
     slot0 = a.sh.prefix_slots;
@@ -720,14 +962,19 @@ decode_partials_kernel(DecodeArgs a) {
   const int hq0 = g * REP;
   T* out = reinterpret_cast<T*>(a.out) + ((size_t)qrow * a.num_q_heads + hq0) * HD;
 
-  if (j >= nsplit) {
+  if (sched ? ctx == 0 : j >= nsplit) {
     if (j == 0 && nps == 0) {  // empty sequence: zeros
       for (int i = tid; i < REP * HD; i += kThreads) out[i] = from_f32<T>(0.f);
+    } else if (j == 0 && a.counters) {
+      // context inside the shared prompt: only the shared pass's partials,
+      // written by the previous launch
+      merge_partials<T, HD, REP>(a, s, hq0, nps, slot0, 0, out,
+                                 reinterpret_cast<float*>(smem) + w * 64, w, lane);
     }
     return;
   }
-  const int t0 = start + j * P;
-  const int t1 = min(ctx, t0 + P);
+  const int t0 = sched ? pc.t0 : start + j * P;
+  const int t1 = sched ? pc.t1 : min(ctx, t0 + P);
   const bool uni = L::uniform(bshift);
 
   const int tbl_entries = L::table_entries(P, bshift);
@@ -748,7 +995,7 @@ decode_partials_kernel(DecodeArgs a) {
   c.scale_log2 = a.scale_log2;
   c.tnew = -1;
   c.knew = c.vnew = nullptr;
-  if (a.k_new && j == nsplit - 1) {
+  if (a.k_new && t1 == ctx) {
     // fused step: this workgroup owns the new token of KV head g
     const int tn = ctx - 1;
     const size_t row_off = ((size_t)s * a.num_kv_heads + g) * HD * G::ISZ;
@@ -883,13 +1130,47 @@ decode_partials_kernel(DecodeArgs a) {
       out[h * HD + d] = from_f32<T>(Ls > 0.f ? O / Ls : 0.f);
     } else {
       const size_t row = ((size_t)s * a.num_q_heads + hq0 + h) * J + slot0 + j;
-      a.ws_o[row * HD + d] = O;
-      if (d == 0) {
-        a.ws_ml[row * 2] = M;
-        a.ws_ml[row * 2 + 1] = Ls;
+      if (a.counters) {
+        // read back in this launch by another workgroup, possibly on another
+        // XCD: device-coherent stores, written through the XCD's L2
+        st_agent(a.ws_o + row * HD + d, O);
+        if (d == 0) {
+          st_agent(a.ws_ml + row * 2, M);
+          st_agent(a.ws_ml + row * 2 + 1, Ls);
+        }
+      } else {
+        a.ws_o[row * HD + d] = O;
+        if (d == 0) {
+          a.ws_ml[row * 2] = M;
+          a.ws_ml[row * 2 + 1] = Ls;
+        }
       }
     }
   }
+  if (!a.counters || (nsplit == 1 && nps == 0)) return;
+
+  // ---- in-launch merge: the last workgroup of (s, g) to count itself merges.
+  // Each wave waits until its device-coherent partial stores are complete
+  // before the barrier; only then is the workgroup counted, so a workgroup
+  // that sees the full count reads every partial back with device-coherent
+  // loads. (No cache-wide write-back or invalidate is needed: the partials
+  // never sit dirty in an L2, and the loads do not take stale L2 lines.)
+  wait_vmcnt<0>();
+  int* last = reinterpret_cast<int*>(smem) + kWaves * 64;
+  __syncthreads();
+  if (nsplit > 1) {
+    if (tid == 0) {
+      int* cnt = a.counters + (size_t)s * a.num_kv_heads + g;
+      const int before = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *last = before == nsplit - 1;
+      // every split has counted: reset for the next launch
+      if (before == nsplit - 1) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!*last) return;
+  }
+  merge_partials<T, HD, REP>(a, s, hq0, nps, slot0, nsplit, out,
+                             reinterpret_cast<float*>(smem) + w * 64, w, lane);
 }
 
 // Merge split partials of sequences with more than one split: one wave per
@@ -905,7 +1186,10 @@ __global__ void __launch_bounds__(64) decode_reduce_kernel(DecodeArgs a, int hea
   const int J = a.num_splits;
   // partials: slots 0 .. nps-1 (shared pass), then slot0 .. slot0+nsplit-1
   int nps = 0, slot0 = 0, nsplit;
-  if (a.sh.group_start) {
+  if (a.sched_q > 0) {
+    const PieceCounts c = piece_counts(ctx, P, a.sched_q);
+    nsplit = ctx > 0 ? c.big + c.small + c.rest : 0;
+  } else if (a.sh.group_start) {
     const int start = min(ctx, shared_len(a.sh, group_of(a.sh, s), lim, a.block_shift));
     nps = (start + a.sh.prefix_part - 1) / a.sh.prefix_part;
     slot0 = a.sh.prefix_slots;
@@ -945,7 +1229,12 @@ pkv_status launch_split(const DecodeArgs& a, hipStream_t st) {
   const int lds = L::bytes(L::table_entries(a.partition, a.block_shift));
   // shared-prefix decode: the leading slots belong to the shared pass
   dim3 grid(a.num_kv_heads, a.num_seqs, a.num_splits - a.sh.prefix_slots);
-  if (a.cu_q) {
+  if (a.sched_q > 0) {
+    // pieces: at most num_splits per sequence
+    const int planes = a.num_seqs * a.num_splits;
+    const int y = planes < kRowGridZ ? planes : kRowGridZ;
+    grid = dim3(a.num_kv_heads, y, (planes + y - 1) / y);
+  } else if (a.cu_q) {
     const int z = a.total_q < kRowGridZ ? a.total_q : kRowGridZ;
     grid = dim3(a.num_kv_heads, (a.total_q + z - 1) / z, z);
   }

@@ -76,7 +76,36 @@ struct DecodeArgs {
   const void* k_new;
   const void* v_new;
   SharedDesc sh;
+  // In-launch merge: when set, every workgroup of a sequence with more than
+  // one partial counts itself in counters[s * Hkv + g] after writing its
+  // partial; the last one merges the sequence's partials for KV head g and
+  // sets the counter back to zero. Must be zero when the launch starts.
+  int32_t* counters;
+  // Piece schedule (sched_q > 0; no shared prefix, no prefill rows, at most
+  // kSchedMaxSeqs sequences): each sequence's context is cut into full pieces
+  // of `partition` tokens, then full pieces of sched_q tokens, then the rest;
+  // the grid's (y, z) plane enumerates all full large pieces, then all full
+  // small pieces, then the rests, so that every workgroup stream is made of
+  // equal pieces and no empty workgroup precedes a live one. Each workgroup
+  // derives its piece from context_lens by a workgroup scan.
+  int32_t sched_q;
 };
+constexpr int kSchedMaxSeqs = 1024;   // 4 sequences per thread of the scan
+
+// Pieces of a context of L tokens under the piece schedule: full pieces of P
+// tokens, full pieces of Q tokens of the rest, then one piece for what is
+// left (an empty context is one empty piece).
+struct PieceCounts {
+  int big, small, rest;
+};
+__host__ __device__ inline PieceCounts piece_counts(int L, int P, int Q) {
+  PieceCounts c;
+  c.big = L / P;
+  const int r = L - c.big * P;
+  c.small = r / Q;
+  c.rest = (r - c.small * Q) > 0 || L == 0;
+  return c;
+}
 constexpr int kRowGridZ = 32768;   // rows per grid z-extent in prefill-row launches
 // Token tile per wave for a row of `row_bytes` (K or V of one KV head).
 int decode_tile_tokens(int row_bytes);
@@ -145,6 +174,30 @@ __device__ __forceinline__ float xor32(float x) {
   return __builtin_bit_cast(float, __shfl_xor(__builtin_bit_cast(int, x), 32));
 }
 
+// x (op) x of lane i ^ 16, and of lane i ^ 32, in VALU cross-lane moves:
+// v_permlane16_swap / v_permlane32_swap of x with x leave rows 0 and 2
+// (lanes 0-31) in one result and rows 1 and 3 (lanes 32-63) in the other, so
+// one op joins each lane's row (half) with its partner's. The sum is the same
+// in both lanes of a pair (addition commutes). The two results are taken out
+// of the returned vector as scalars before any bit cast (a bit cast of a
+// vector element reads the vector's first element).
+template <bool MAX>
+__device__ __forceinline__ float join16(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  const float a = __uint_as_float(r0), b = __uint_as_float(r1);
+  return MAX ? fmaxf(a, b) : a + b;
+}
+template <bool MAX>
+__device__ __forceinline__ float join32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  const float a = __uint_as_float(r0), b = __uint_as_float(r1);
+  return MAX ? fmaxf(a, b) : a + b;
+}
+
 // Sum over aligned groups of W consecutive lanes; every lane gets its group's sum.
 template <int W>
 __device__ __forceinline__ float group_sum(float x) {
@@ -152,8 +205,8 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (W >= 4) x += dpp<kQuadXor2>(x);
   if constexpr (W >= 8) x += dpp<kRowHalfMirror>(x);
   if constexpr (W >= 16) x += dpp<kRowMirror>(x);
-  if constexpr (W >= 32) x += swz_xor16(x);
-  if constexpr (W >= 64) x += xor32(x);
+  if constexpr (W >= 32) x = join16<false>(x);
+  if constexpr (W >= 64) x = join32<false>(x);
   return x;
 }
 
@@ -165,8 +218,8 @@ __device__ __forceinline__ float strided_sum(float x) {
   if constexpr (STRIDE <= 2) x += dpp<kRowRor + 2>(x);
   if constexpr (STRIDE <= 4) x += dpp<kRowRor + 4>(x);
   if constexpr (STRIDE <= 8) x += dpp<kRowRor + 8>(x);
-  if constexpr (STRIDE <= 16) x += swz_xor16(x);
-  if constexpr (STRIDE <= 32) x += xor32(x);
+  if constexpr (STRIDE <= 16) x = join16<false>(x);
+  if constexpr (STRIDE <= 32) x = join32<false>(x);
   return x;
 }
 
@@ -177,8 +230,8 @@ __device__ __forceinline__ float group_max(float x) {
   if constexpr (W >= 4) x = fmaxf(x, dpp<kQuadXor2>(x));
   if constexpr (W >= 8) x = fmaxf(x, dpp<kRowHalfMirror>(x));
   if constexpr (W >= 16) x = fmaxf(x, dpp<kRowMirror>(x));
-  if constexpr (W >= 32) x = fmaxf(x, swz_xor16(x));
-  if constexpr (W >= 64) x = fmaxf(x, xor32(x));
+  if constexpr (W >= 32) x = join16<true>(x);
+  if constexpr (W >= 64) x = join32<true>(x);
   return x;
 }
 

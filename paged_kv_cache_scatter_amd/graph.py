@@ -45,7 +45,7 @@ class LayerSteps:
         self.partition = partition or _b.decode_partition(S, self.max_ctx, k_pools[0])
         nws = _b.decode_workspace_bytes(S, Hq, self.max_ctx, k_pools[0], self.partition)
         # one workspace serves every layer: the layers run in stream order
-        self.ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=q.device)
+        self.ws = torch.zeros(max(nws, 16), dtype=torch.uint8, device=q.device)
         self.out = torch.empty_like(q)
         self.graph = None
 

@@ -63,7 +63,7 @@ def test_partition_sweep(cfg, S, parts):
     p = parts[0]
     both = to_host(pc.decode(partition=p))
     out = torch.empty_like(pc.q)
-    ws = torch.empty(pkv.decode_workspace_bytes(pc.wl.num_seqs, pc.wl.num_q_heads, pc.max_ctx,
+    ws = torch.zeros(pkv.decode_workspace_bytes(pc.wl.num_seqs, pc.wl.num_q_heads, pc.max_ctx,
                                                 pc.k_pool, p) or 1,
                      dtype=torch.uint8, device=pc.q.device)
     for ph in ("partials", "reduce"):

@@ -48,7 +48,7 @@ def _fused(pc, rows, partition, phase="both"):
                               pc.v_pool, pc.tables, pc.ctx, wl.scale, pc.max_ctx,
                               partition=partition)
     else:
-        ws = torch.empty(max(16, pkv.decode_workspace_bytes(wl.num_seqs, wl.num_q_heads,
+        ws = torch.zeros(max(16, pkv.decode_workspace_bytes(wl.num_seqs, wl.num_q_heads,
                                                             pc.max_ctx, pc.k_pool, partition)),
                          dtype=torch.uint8, device=pc.q.device)
         out = torch.empty_like(pc.q)
