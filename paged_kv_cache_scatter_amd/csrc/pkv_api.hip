@@ -59,6 +59,7 @@ struct DecodePlan {
   int partition = 0;
   int splits = 0;       // partial slots per (sequence, head)
   int sched_q = 0;      // small piece of the piece schedule (0: plain split grid)
+  int sched_align = 0;
   size_t ws_ml_bytes = 0;
   size_t ws_cnt_offset = 0;   // merge counters [S, Hkv] int32, after the partials
   size_t ws_bytes = 0;
@@ -154,14 +155,16 @@ pkv_status plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks
   plan->splits = splits;
   plan->sched_q = 0;
   if (splits > 1 && allow_sched && num_seqs <= kSchedMaxSeqs) {
-    // piece schedule: full pieces of `part` tokens, then of half of it
-    // (rounded to the alignment), then each sequence's rest. Measured on the
-    // LLaMA-2-70B-layer workload (1024-token pieces): halves 140 us,
-    // quarters 141 us, eighths 150 us; no small pieces 149 us.
+    // piece schedule: full pieces of `part` tokens, the rest in one or two
+    // tail pieces of about half of it (rounded to the alignment), a short
+    // rest joining the last full piece. Measured on the LLaMA-2-70B-layer
+    // workload (1024-token pieces): tails of about 512 tokens 140 us, 256
+    // 141 us, 128 150 us; no tail pieces 149 us.
     const int q = std::max(align, (part / 2) / align * align);
-    const int64_t J = (int64_t)max_ctx / part + (part - 1) / q + 1;
-    if (J <= kMaxSplits) {
+    const int64_t J = (int64_t)max_ctx / part + part / q + 1;
+    if (J <= kMaxSplits && max_piece(part, q) <= kMaxPartition) {
       plan->sched_q = q;
+      plan->sched_align = align;
       plan->splits = (int)J;
     }
   }
@@ -299,6 +302,7 @@ pkv_status decode_impl(Phase phase, const void* q, int32_t num_seqs, int32_t num
   a.partition = plan.partition;
   a.num_splits = plan.splits;
   a.sched_q = plan.sched_q;
+  a.sched_align = plan.sched_align;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.cu_q = nullptr;
   a.total_q = 0;

@@ -789,90 +789,71 @@ struct Piece {
 
 // Piece number `pid` of the schedule (see DecodeArgs::sched_q): every thread
 // counts the pieces of four consecutive sequences, a workgroup scan gives
-// each thread its offsets in the three segments (full large pieces, full
-// small pieces, rests), and the thread holding the piece publishes it.
-// Returns false (uniformly) when pid is past the last piece. `lds` holds at
-// least 32 ints; the caller synchronises before reusing it.
+// each thread its offsets among the large and among the tail pieces, and the
+// thread holding the piece publishes it. Returns false (uniformly) when pid
+// is past the last piece. `lds` holds at least 32 ints; the caller
+// synchronises before reusing it.
 __device__ __forceinline__ bool find_piece(const DecodeArgs& a, int pid, int lim, Piece& pc,
-                                        int* lds) {
+                                           int* lds) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int P = a.partition, Q = a.sched_q;
+  const int P = a.partition, Q = a.sched_q, A = a.sched_align;
   int L[4];
   PieceCounts pcs[4];
-  uint32_t nbig = 0, nsr = 0;   // large pieces; (small << 16) | rests
+  uint32_t nbig = 0, ntail = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int sq = tid * 4 + i;
     int c = sq < a.num_seqs ? a.ctx_lens[sq] : 0;
     c = c < 0 ? 0 : (c > lim ? lim : c);
     L[i] = c;
-    pcs[i] = sq < a.num_seqs ? piece_counts(c, P, Q) : PieceCounts{0, 0, 0};
+    pcs[i] = sq < a.num_seqs ? piece_counts(c, P, Q, A) : PieceCounts{0, 0, 0};
     nbig += pcs[i].big;
-    nsr += ((uint32_t)pcs[i].small << 16) | (uint32_t)pcs[i].rest;
+    ntail += pcs[i].tail;
   }
-  const uint32_t ib = wave_incl_scan(nbig), is = wave_incl_scan(nsr);
+  const uint32_t ib = wave_incl_scan(nbig), it = wave_incl_scan(ntail);
   if (lane == 63) {
     lds[w] = (int)ib;
-    lds[4 + w] = (int)is;
+    lds[4 + w] = (int)it;
   }
   lds[16] = -1;
   __syncthreads();
-  uint32_t pb = 0, ps = 0, tb = 0, ts = 0;
+  uint32_t pb = 0, pt = 0, tb = 0, tt = 0;
 #pragma unroll
   for (int k = 0; k < kWaves; ++k) {
-    const uint32_t vb = (uint32_t)lds[k], vs = (uint32_t)lds[4 + k];
+    const uint32_t vb = (uint32_t)lds[k], vt = (uint32_t)lds[4 + k];
     if (k < w) {
       pb += vb;
-      ps += vs;
+      pt += vt;
     }
     tb += vb;
-    ts += vs;
+    tt += vt;
   }
-  const uint32_t eb = pb + ib - nbig;   // large pieces before this thread's
-  const uint32_t es = ps + is - nsr;
-  const uint32_t tsmall = ts >> 16, trest = ts & 0xFFFF;
   const uint32_t u = (uint32_t)pid;
-  // segment of pid and its index within the segment
-  int seg;
-  uint32_t k;
-  if (u < tb) {
-    seg = 0;
-    k = u - eb;
-  } else if (u < tb + tsmall) {
-    seg = 1;
-    k = u - tb - (es >> 16);
-  } else if (u < tb + tsmall + trest) {
-    seg = 2;
-    k = u - tb - tsmall - (es & 0xFFFF);
-  } else {
-    return false;
-  }
-  const uint32_t mine = seg == 0 ? nbig : seg == 1 ? (nsr >> 16) : (nsr & 0xFFFF);
-  if (k < mine) {   // this thread holds the piece (unsigned: k < 0 wraps)
+  if (u >= tb + tt) return false;
+  const bool big = u < tb;
+  // index among this thread's pieces of the segment (unsigned: below wraps)
+  uint32_t k = big ? u - (pb + ib - nbig) : u - tb - (pt + it - ntail);
+  if (k < (big ? nbig : ntail)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t ni = seg == 0 ? pcs[i].big : seg == 1 ? pcs[i].small : pcs[i].rest;
+      const PieceCounts& c = pcs[i];
+      const uint32_t ni = big ? c.big : c.tail;
       if (k < ni) {
-        const PieceCounts& c = pcs[i];
         int t0, t1, slot;
-        if (seg == 0) {
+        if (big) {
           t0 = (int)k * P;
-          t1 = t0 + P;
+          t1 = ((int)k == c.big - 1 && c.tail == 0) ? L[i] : t0 + P;
           slot = (int)k;
-        } else if (seg == 1) {
-          t0 = c.big * P + (int)k * Q;
-          t1 = t0 + Q;
-          slot = c.big + (int)k;
         } else {
-          t0 = c.big * P + c.small * Q;
-          t1 = L[i];
-          slot = c.big + c.small;
+          t0 = c.big * P + (int)k * c.base;
+          t1 = ((int)k == c.tail - 1) ? L[i] : t0 + c.base;
+          slot = c.big + (int)k;
         }
         lds[16] = tid * 4 + i;
         lds[17] = t0;
         lds[18] = t1;
         lds[19] = slot;
-        lds[20] = c.big + c.small + c.rest;
+        lds[20] = c.big + c.tail;
         lds[21] = L[i];
         break;
       }
@@ -977,7 +958,7 @@ decode_partials_kernel(DecodeArgs a) {
   const int t1 = sched ? pc.t1 : min(ctx, t0 + P);
   const bool uni = L::uniform(bshift);
 
-  const int tbl_entries = L::table_entries(P, bshift);
+  const int tbl_entries = L::table_entries(sched ? max_piece(P, a.sched_q) : P, bshift);
   int* tbl = reinterpret_cast<int*>(smem);
   int* idslot = reinterpret_cast<int*>(smem + round16(tbl_entries * 4)) + w * L::kWaveWords;
   uint32_t* pbuf = reinterpret_cast<uint32_t*>(idslot + 128);
@@ -1187,8 +1168,8 @@ __global__ void __launch_bounds__(64) decode_reduce_kernel(DecodeArgs a, int hea
   // partials: slots 0 .. nps-1 (shared pass), then slot0 .. slot0+nsplit-1
   int nps = 0, slot0 = 0, nsplit;
   if (a.sched_q > 0) {
-    const PieceCounts c = piece_counts(ctx, P, a.sched_q);
-    nsplit = ctx > 0 ? c.big + c.small + c.rest : 0;
+    const PieceCounts c = piece_counts(ctx, P, a.sched_q, a.sched_align);
+    nsplit = ctx > 0 ? c.big + c.tail : 0;
   } else if (a.sh.group_start) {
     const int start = min(ctx, shared_len(a.sh, group_of(a.sh, s), lim, a.block_shift));
     nps = (start + a.sh.prefix_part - 1) / a.sh.prefix_part;
@@ -1226,7 +1207,8 @@ __global__ void __launch_bounds__(64) decode_reduce_kernel(DecodeArgs a, int hea
 template <typename T, int HD, int REP>
 pkv_status launch_split(const DecodeArgs& a, hipStream_t st) {
   using L = Lds<T, HD, REP>;
-  const int lds = L::bytes(L::table_entries(a.partition, a.block_shift));
+  const int piece = a.sched_q > 0 ? max_piece(a.partition, a.sched_q) : a.partition;
+  const int lds = L::bytes(L::table_entries(piece, a.block_shift));
   // shared-prefix decode: the leading slots belong to the shared pass
   dim3 grid(a.num_kv_heads, a.num_seqs, a.num_splits - a.sh.prefix_slots);
   if (a.sched_q > 0) {

@@ -82,30 +82,42 @@ struct DecodeArgs {
   // sets the counter back to zero. Must be zero when the launch starts.
   int32_t* counters;
   // Piece schedule (sched_q > 0; no shared prefix, no prefill rows, at most
-  // kSchedMaxSeqs sequences): each sequence's context is cut into full pieces
-  // of `partition` tokens, then full pieces of sched_q tokens, then the rest;
-  // the grid's (y, z) plane enumerates all full large pieces, then all full
-  // small pieces, then the rests, so that every workgroup stream is made of
-  // equal pieces and no empty workgroup precedes a live one. Each workgroup
-  // derives its piece from context_lens by a workgroup scan.
+  // kSchedMaxSeqs sequences): each sequence's context is cut into pieces by
+  // piece_counts; the grid's (y, z) plane enumerates all large pieces, then
+  // all tail pieces, so that every workgroup stream is made of near-equal
+  // pieces, the last ones short, and no empty workgroup precedes a live one.
+  // Each workgroup derives its piece from context_lens by a workgroup scan.
   int32_t sched_q;
+  int32_t sched_align;   // piece starts are multiples of it
 };
 constexpr int kSchedMaxSeqs = 1024;   // 4 sequences per thread of the scan
 
-// Pieces of a context of L tokens under the piece schedule: full pieces of P
-// tokens, full pieces of Q tokens of the rest, then one piece for what is
-// left (an empty context is one empty piece).
+// Pieces of a context of L tokens under the piece schedule (P large, Q small
+// piece, starts aligned to A): full pieces of P tokens, the last of which
+// also takes a rest shorter than Q / 2; a longer rest, or a context shorter
+// than P, is cut into tail = max(1, round(rest / Q)) pieces of `base` tokens
+// (a multiple of A), the last taking what is left. An empty context is one
+// empty tail piece.
 struct PieceCounts {
-  int big, small, rest;
+  int big, tail, base;
 };
-__host__ __device__ inline PieceCounts piece_counts(int L, int P, int Q) {
+__host__ __device__ inline PieceCounts piece_counts(int L, int P, int Q, int A) {
   PieceCounts c;
   c.big = L / P;
   const int r = L - c.big * P;
-  c.small = r / Q;
-  c.rest = (r - c.small * Q) > 0 || L == 0;
+  if (c.big > 0 && 2 * r < Q) {
+    c.tail = 0;
+    c.base = 0;
+  } else {
+    c.tail = (r + Q / 2) / Q;
+    c.tail = c.tail < 1 ? 1 : c.tail;
+    c.base = (r / c.tail) / A * A;
+    if (c.base == 0) c.tail = 1;
+  }
   return c;
 }
+// Longest piece the schedule makes (bounds the per-lane path's table slice).
+__host__ __device__ inline int max_piece(int P, int Q) { return P + Q / 2; }
 constexpr int kRowGridZ = 32768;   // rows per grid z-extent in prefill-row launches
 // Token tile per wave for a row of `row_bytes` (K or V of one KV head).
 int decode_tile_tokens(int row_bytes);
