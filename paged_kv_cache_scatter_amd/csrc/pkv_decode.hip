@@ -789,26 +789,27 @@ struct Piece {
 
 // Piece number `pid` of the schedule (see DecodeArgs::sched_q): every thread
 // counts the pieces of four consecutive sequences, a workgroup scan gives
-// each thread its offsets among the large and among the tail pieces, and the
-// thread holding the piece publishes it. Returns false (uniformly) when pid
-// is past the last piece. `lds` holds at least 32 ints; the caller
-// synchronises before reusing it.
+// each thread its offsets among the large pieces, the long tail pieces and
+// the short tail pieces (the order they run in), and the thread holding the
+// piece publishes it. Returns false (uniformly) when pid is past the last
+// piece. `lds` holds at least 32 ints; the caller synchronises before
+// reusing it.
 __device__ __forceinline__ bool find_piece(const DecodeArgs& a, int pid, int lim, Piece& pc,
                                            int* lds) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int P = a.partition, Q = a.sched_q, A = a.sched_align;
   int L[4];
   PieceCounts pcs[4];
-  uint32_t nbig = 0, ntail = 0;
+  uint32_t nbig = 0, ntail = 0;   // ntail: (long << 16) | short
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int sq = tid * 4 + i;
     int c = sq < a.num_seqs ? a.ctx_lens[sq] : 0;
     c = c < 0 ? 0 : (c > lim ? lim : c);
     L[i] = c;
-    pcs[i] = sq < a.num_seqs ? piece_counts(c, P, Q, A) : PieceCounts{0, 0, 0};
+    pcs[i] = sq < a.num_seqs ? piece_counts(c, P, Q, A) : PieceCounts{0, 0, 0, 0};
     nbig += pcs[i].big;
-    ntail += pcs[i].tail;
+    ntail += ((uint32_t)pcs[i].nlong << 16) | (uint32_t)(pcs[i].tail - pcs[i].nlong);
   }
   const uint32_t ib = wave_incl_scan(nbig), it = wave_incl_scan(ntail);
   if (lane == 63) {
@@ -828,26 +829,44 @@ __device__ __forceinline__ bool find_piece(const DecodeArgs& a, int pid, int lim
     tb += vb;
     tt += vt;
   }
+  const uint32_t tlong = tt >> 16, tshort = tt & 0xFFFF;
+  const uint32_t et = pt + it - ntail;   // this thread's packed tail offsets
   const uint32_t u = (uint32_t)pid;
-  if (u >= tb + tt) return false;
-  const bool big = u < tb;
-  // index among this thread's pieces of the segment (unsigned: below wraps)
-  uint32_t k = big ? u - (pb + ib - nbig) : u - tb - (pt + it - ntail);
-  if (k < (big ? nbig : ntail)) {
+  if (u >= tb + tlong + tshort) return false;
+  // segment (0 large, 1 long tail, 2 short tail) and index among this
+  // thread's pieces of it (unsigned: an index below the thread's wraps)
+  const int seg = u < tb ? 0 : u < tb + tlong ? 1 : 2;
+  uint32_t k = seg == 0 ? u - (pb + ib - nbig)
+             : seg == 1 ? u - tb - (et >> 16)
+                        : u - tb - tlong - (et & 0xFFFF);
+  const uint32_t mine = seg == 0 ? nbig : seg == 1 ? (ntail >> 16) : (ntail & 0xFFFF);
+  if (k < mine) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const PieceCounts& c = pcs[i];
-      const uint32_t ni = big ? c.big : c.tail;
+      const uint32_t ni = seg == 0 ? c.big : seg == 1 ? c.nlong : c.tail - c.nlong;
       if (k < ni) {
-        int t0, t1, slot;
-        if (big) {
+        int t0 = 0, t1 = 0, slot = 0;
+        if (seg == 0) {
           t0 = (int)k * P;
           t1 = ((int)k == c.big - 1 && c.tail == 0) ? L[i] : t0 + P;
           slot = (int)k;
         } else {
-          t0 = c.big * P + (int)k * c.base;
-          t1 = ((int)k == c.tail - 1) ? L[i] : t0 + c.base;
-          slot = c.big + (int)k;
+          // the k-th tail piece of this class, in piece order
+          int left = (int)k;
+          for (int j = 0; j < c.tail; ++j) {
+            const int a0 = c.big * P + j * c.base;
+            const int a1 = j == c.tail - 1 ? L[i] : a0 + c.base;
+            if (long_tail(a1 - a0, Q) == (seg == 1)) {
+              if (left == 0) {
+                t0 = a0;
+                t1 = a1;
+                slot = c.big + j;
+                break;
+              }
+              --left;
+            }
+          }
         }
         lds[16] = tid * 4 + i;
         lds[17] = t0;

@@ -95,12 +95,14 @@ constexpr int kSchedMaxSeqs = 1024;   // 4 sequences per thread of the scan
 // Pieces of a context of L tokens under the piece schedule (P large, Q small
 // piece, starts aligned to A): full pieces of P tokens, the last of which
 // also takes a rest shorter than Q / 2; a longer rest, or a context shorter
-// than P, is cut into tail = max(1, round(rest / Q)) pieces of `base` tokens
-// (a multiple of A), the last taking what is left. An empty context is one
-// empty tail piece.
+// than P, is cut into tail = ceil(rest / Q) pieces of `base` tokens (a
+// multiple of A), the last taking what is left. An empty context is one
+// empty tail piece. Tail pieces of at least 3/4 Q are "long": the schedule
+// runs them before the short ones.
 struct PieceCounts {
-  int big, tail, base;
+  int big, tail, base, nlong;
 };
+__host__ __device__ inline bool long_tail(int len, int Q) { return 4 * len >= 3 * Q; }
 __host__ __device__ inline PieceCounts piece_counts(int L, int P, int Q, int A) {
   PieceCounts c;
   c.big = L / P;
@@ -108,11 +110,14 @@ __host__ __device__ inline PieceCounts piece_counts(int L, int P, int Q, int A) 
   if (c.big > 0 && 2 * r < Q) {
     c.tail = 0;
     c.base = 0;
+    c.nlong = 0;
   } else {
-    c.tail = (r + Q / 2) / Q;
+    c.tail = (r + Q - 1) / Q;
     c.tail = c.tail < 1 ? 1 : c.tail;
     c.base = (r / c.tail) / A * A;
     if (c.base == 0) c.tail = 1;
+    const int last = r - (c.tail - 1) * c.base;
+    c.nlong = (long_tail(c.base, Q) ? c.tail - 1 : 0) + (long_tail(last, Q) ? 1 : 0);
   }
   return c;
 }

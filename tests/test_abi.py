@@ -85,11 +85,11 @@ def test_decode_argument_errors(lib):
 
 def test_workspace_bytes(lib):
     d = _desc(nb=32769, bs=16, hkv=8, hd=128)
-    # 64 sequences x 64 heads x 11 partial slots: a context of up to 8192
-    # tokens has at most 8 pieces of 1024 tokens and 2 tail pieces of about
-    # 512 (slots: 8192 / 1024 + 1024 / 512 + 1); (m, l) then o[128], then one
-    # merge counter per (sequence, KV head), each part 256-byte aligned
-    rows = 64 * 64 * 11
+    # 64 sequences x 64 heads x 10 partial slots: a context of up to 8192
+    # tokens has at most 8 pieces of 1024 tokens and 2 tail pieces of at most
+    # 512 (slots: 8192 / 1024 + ceil(1023 / 512)); (m, l) then o[128], then
+    # one merge counter per (sequence, KV head), each part 256-byte aligned
+    rows = 64 * 64 * 10
     assert lib.pkv_decode_workspace_bytes(64, 64, 8192, 1024, ctypes.byref(d)) == \
         rows * 2 * 4 + rows * 128 * 4 + 64 * 8 * 4
     assert lib.pkv_decode_workspace_bytes(64, 64, 1024, 1024, ctypes.byref(d)) == 0
