@@ -154,13 +154,13 @@ pkv_status plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks
   plan->partition = part;
   plan->splits = splits;
   plan->sched_q = 0;
-  if (splits > 1 && allow_sched && num_seqs <= kSchedMaxSeqs) {
+  if (splits > 1 && allow_sched && num_seqs <= kSchedMaxSeqs && is_pow2(part) && is_pow2(align)) {
     // piece schedule: full pieces of `part` tokens, the rest in tail pieces
     // of at most half of it (rounded to the alignment), a short rest joining
     // the last full piece. Measured on the LLaMA-2-70B-layer workload
     // (1024-token pieces): tails of about 512 tokens 140 us, 256 141 us, 128
     // 150 us; no tail pieces 149 us.
-    const int q = std::max(align, (part / 2) / align * align);
+    const int q = std::max(align, part / 2);   // powers of two: a multiple of align
     const int64_t J = (int64_t)max_ctx / part + (part - 1 + q - 1) / q;
     if (J <= kMaxSplits && max_piece(part, q) <= kMaxPartition) {
       plan->sched_q = q;

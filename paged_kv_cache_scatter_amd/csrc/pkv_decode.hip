@@ -797,17 +797,22 @@ struct Piece {
 __device__ __forceinline__ bool find_piece(const DecodeArgs& a, int pid, int lim, Piece& pc,
                                            int* lds) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int P = a.partition, Q = a.sched_q, A = a.sched_align;
+  const int P = a.partition;
+  const int lp = __builtin_ctz((unsigned)P), lq = __builtin_ctz((unsigned)a.sched_q),
+            la = __builtin_ctz((unsigned)a.sched_align);
   int L[4];
   PieceCounts pcs[4];
   uint32_t nbig = 0, ntail = 0;   // ntail: (long << 16) | short
 #pragma unroll
+  for (int i = 0; i < 4; ++i) {   // all four loads in flight together
+    const int sq = tid * 4 + i;
+    L[i] = sq < a.num_seqs ? a.ctx_lens[sq] : 0;
+  }
+#pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int sq = tid * 4 + i;
-    int c = sq < a.num_seqs ? a.ctx_lens[sq] : 0;
-    c = c < 0 ? 0 : (c > lim ? lim : c);
-    L[i] = c;
-    pcs[i] = sq < a.num_seqs ? piece_counts(c, P, Q, A) : PieceCounts{0, 0, 0, 0};
+    L[i] = L[i] < 0 ? 0 : (L[i] > lim ? lim : L[i]);
+    pcs[i] = sq < a.num_seqs ? piece_counts(L[i], lp, lq, la) : PieceCounts{0, 0, 0, 0};
     nbig += pcs[i].big;
     ntail += ((uint32_t)pcs[i].nlong << 16) | (uint32_t)(pcs[i].tail - pcs[i].nlong);
   }
@@ -857,7 +862,7 @@ __device__ __forceinline__ bool find_piece(const DecodeArgs& a, int pid, int lim
           for (int j = 0; j < c.tail; ++j) {
             const int a0 = c.big * P + j * c.base;
             const int a1 = j == c.tail - 1 ? L[i] : a0 + c.base;
-            if (long_tail(a1 - a0, Q) == (seg == 1)) {
+            if (long_tail(a1 - a0, lq) == (seg == 1)) {
               if (left == 0) {
                 t0 = a0;
                 t1 = a1;
@@ -1187,7 +1192,9 @@ __global__ void __launch_bounds__(64) decode_reduce_kernel(DecodeArgs a, int hea
   // partials: slots 0 .. nps-1 (shared pass), then slot0 .. slot0+nsplit-1
   int nps = 0, slot0 = 0, nsplit;
   if (a.sched_q > 0) {
-    const PieceCounts c = piece_counts(ctx, P, a.sched_q, a.sched_align);
+    const PieceCounts c = piece_counts(ctx, __builtin_ctz((unsigned)P),
+                                       __builtin_ctz((unsigned)a.sched_q),
+                                       __builtin_ctz((unsigned)a.sched_align));
     nsplit = ctx > 0 ? c.big + c.tail : 0;
   } else if (a.sh.group_start) {
     const int start = min(ctx, shared_len(a.sh, group_of(a.sh, s), lim, a.block_shift));

@@ -87,37 +87,38 @@ struct DecodeArgs {
   // all tail pieces, so that every workgroup stream is made of near-equal
   // pieces, the last ones short, and no empty workgroup precedes a live one.
   // Each workgroup derives its piece from context_lens by a workgroup scan.
-  int32_t sched_q;
-  int32_t sched_align;   // piece starts are multiples of it
+  int32_t sched_q;       // small piece (tokens); partition and sched_q are powers of two
+  int32_t sched_align;   // piece starts are multiples of it (a power of two)
 };
 constexpr int kSchedMaxSeqs = 1024;   // 4 sequences per thread of the scan
 
 // Pieces of a context of L tokens under the piece schedule (P large, Q small
-// piece, starts aligned to A): full pieces of P tokens, the last of which
-// also takes a rest shorter than Q / 2; a longer rest, or a context shorter
-// than P, is cut into tail = ceil(rest / Q) pieces of `base` tokens (a
-// multiple of A), the last taking what is left. An empty context is one
-// empty tail piece. Tail pieces of at least 3/4 Q are "long": the schedule
-// runs them before the short ones.
+// piece, starts aligned to A; all three powers of two with A <= Q <= P and
+// Q >= P / 2, given as log2: lp, lq, la): full pieces of P tokens, the last
+// of which also takes a rest shorter than Q / 2; a longer rest, or a context
+// shorter than P, is cut into tail = ceil(rest / Q) (1 or 2) pieces of
+// `base` tokens (a multiple of A), the last taking what is left. An empty
+// context is one empty tail piece. Tail pieces of at least 3/4 Q are "long":
+// the schedule runs them before the short ones.
 struct PieceCounts {
   int big, tail, base, nlong;
 };
-__host__ __device__ inline bool long_tail(int len, int Q) { return 4 * len >= 3 * Q; }
-__host__ __device__ inline PieceCounts piece_counts(int L, int P, int Q, int A) {
+__host__ __device__ inline bool long_tail(int len, int lq) { return 4 * len >= (3 << lq); }
+__host__ __device__ inline PieceCounts piece_counts(int L, int lp, int lq, int la) {
   PieceCounts c;
-  c.big = L / P;
-  const int r = L - c.big * P;
-  if (c.big > 0 && 2 * r < Q) {
+  c.big = L >> lp;
+  const int r = L - (c.big << lp);
+  if (c.big > 0 && 2 * r < (1 << lq)) {
     c.tail = 0;
     c.base = 0;
     c.nlong = 0;
   } else {
-    c.tail = (r + Q - 1) / Q;
+    c.tail = (r + (1 << lq) - 1) >> lq;
     c.tail = c.tail < 1 ? 1 : c.tail;
-    c.base = (r / c.tail) / A * A;
+    c.base = ((r >> (c.tail - 1)) >> la) << la;
     if (c.base == 0) c.tail = 1;
     const int last = r - (c.tail - 1) * c.base;
-    c.nlong = (long_tail(c.base, Q) ? c.tail - 1 : 0) + (long_tail(last, Q) ? 1 : 0);
+    c.nlong = (long_tail(c.base, lq) ? c.tail - 1 : 0) + (long_tail(last, lq) ? 1 : 0);
   }
   return c;
 }
