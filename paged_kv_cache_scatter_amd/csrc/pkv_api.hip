@@ -60,6 +60,7 @@ struct DecodePlan {
   int splits = 0;       // partial slots per (sequence, head)
   int sched_q = 0;      // small piece of the piece schedule (0: plain split grid)
   int sched_align = 0;
+  bool sched_lpt = false;   // one piece per sequence, longest-first
   size_t ws_ml_bytes = 0;
   size_t ws_cnt_offset = 0;   // merge counters [S, Hkv] int32, after the partials
   size_t ws_bytes = 0;
@@ -168,6 +169,8 @@ pkv_status plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks
       plan->splits = (int)J;
     }
   }
+  // single-piece plans: the sequences in longest-first order
+  plan->sched_lpt = plan->splits == 1 && allow_sched && num_seqs <= kSchedMaxSeqs;
   plan->ws_ml_bytes = plan->ws_cnt_offset = plan->ws_bytes = 0;
   if (plan->splits > 1) plan_workspace(num_seqs, num_q_heads, pool, plan->splits, plan);
   return PKV_OK;
@@ -303,6 +306,7 @@ pkv_status decode_impl(Phase phase, const void* q, int32_t num_seqs, int32_t num
   a.num_splits = plan.splits;
   a.sched_q = plan.sched_q;
   a.sched_align = plan.sched_align;
+  a.sched_lpt = plan.sched_lpt;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.cu_q = nullptr;
   a.total_q = 0;

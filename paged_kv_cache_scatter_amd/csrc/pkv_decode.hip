@@ -894,6 +894,92 @@ __device__ __forceinline__ bool find_piece(const DecodeArgs& a, int pid, int lim
   return pc.s >= 0;
 }
 
+// Sequence number `pid` in longest-first order (see DecodeArgs::sched_lpt):
+// every thread classifies four consecutive sequences by length (class
+// floor(kLenClasses * L / (lim + 1)), longest class first), a workgroup scan
+// of the class counts gives each thread its offsets, and the thread holding
+// the sequence publishes it as a one-piece Piece. Returns false (uniformly)
+// when pid is past the last sequence.
+__device__ __forceinline__ bool find_sequence_lpt(const DecodeArgs& a, int pid, int lim,
+                                                  Piece& pc, int* lds) {
+  static_assert(kLenClasses == 4, "two 16-bit class counts per scanned word");
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const float cls_scale = (float)kLenClasses / (float)(lim + 1);
+  int L[4], cls[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {   // all four loads in flight together
+    const int sq = tid * 4 + i;
+    L[i] = sq < a.num_seqs ? a.ctx_lens[sq] : 0;
+  }
+  uint32_t hi = 0, lo = 0;   // counts of segments 0, 1 (hi) and 2, 3 (lo), 16 bits each
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int sq = tid * 4 + i;
+    L[i] = L[i] < 0 ? 0 : (L[i] > lim ? lim : L[i]);
+    int c = (int)((float)L[i] * cls_scale);
+    c = c > kLenClasses - 1 ? kLenClasses - 1 : c;
+    const int seg = kLenClasses - 1 - c;   // longest class is segment 0
+    cls[i] = sq < a.num_seqs ? seg : -1;
+    if (cls[i] >= 0) {
+      if (seg < 2) hi += 1u << (16 * (1 - seg));
+      else lo += 1u << (16 * (3 - seg));
+    }
+  }
+  const uint32_t ih = wave_incl_scan(hi), il = wave_incl_scan(lo);
+  if (lane == 63) {
+    lds[w] = (int)ih;
+    lds[4 + w] = (int)il;
+  }
+  lds[16] = -1;
+  __syncthreads();
+  uint32_t ph = 0, pl = 0, th = 0, tl = 0;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) {
+    const uint32_t vh = (uint32_t)lds[k], vl = (uint32_t)lds[4 + k];
+    if (k < w) {
+      ph += vh;
+      pl += vl;
+    }
+    th += vh;
+    tl += vl;
+  }
+  const uint32_t eh = ph + ih - hi, el = pl + il - lo;   // exclusive, this thread
+  const uint32_t tot[4] = {th >> 16, th & 0xFFFF, tl >> 16, tl & 0xFFFF};
+  const uint32_t exc[4] = {eh >> 16, eh & 0xFFFF, el >> 16, el & 0xFFFF};
+  const uint32_t mine[4] = {hi >> 16, hi & 0xFFFF, lo >> 16, lo & 0xFFFF};
+  uint32_t u = (uint32_t)pid;
+  int seg = 0;
+#pragma unroll
+  for (int c = 0; c < kLenClasses - 1; ++c) {
+    if (seg == c && u >= tot[c]) {
+      u -= tot[c];
+      seg = c + 1;
+    }
+  }
+  if (u >= tot[seg]) return false;
+  uint32_t k = u - exc[seg];
+  if (k < mine[seg]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (cls[i] == seg) {
+        if (k == 0) {
+          lds[16] = tid * 4 + i;
+          lds[17] = L[i];
+          break;
+        }
+        --k;
+      }
+    }
+  }
+  __syncthreads();
+  pc.s = lds[16];
+  pc.t0 = 0;
+  pc.t1 = pc.ctx = lds[17];
+  pc.slot = 0;
+  pc.n = 1;
+  return pc.s >= 0;
+}
+
 template <typename T, int HD, int REP>
 __global__ void __launch_bounds__(kThreads)
 decode_partials_kernel(DecodeArgs a) {
@@ -914,10 +1000,12 @@ decode_partials_kernel(DecodeArgs a) {
   int ctx;
   // piece schedule: this workgroup's sequence, token range and partial slot
   Piece pc{};
-  const bool sched = a.sched_q > 0;
+  const bool sched = a.sched_q > 0 || a.sched_lpt;
   if (sched) {
-    if (!find_piece(a, blockIdx.y + gridDim.y * blockIdx.z, lim, pc,
-                    reinterpret_cast<int*>(smem)))
+    const int pid = blockIdx.y + gridDim.y * blockIdx.z;
+    int* scan_lds = reinterpret_cast<int*>(smem);
+    if (a.sched_lpt ? !find_sequence_lpt(a, pid, lim, pc, scan_lds)
+                    : !find_piece(a, pid, lim, pc, scan_lds))
       return;
     // memory safety whatever the scan gave: an inconsistent piece does no work
     if ((unsigned)pc.s >= (unsigned)a.num_seqs || pc.t0 < 0 || pc.t0 > pc.t1 ||
@@ -982,7 +1070,7 @@ decode_partials_kernel(DecodeArgs a) {
   const int t1 = sched ? pc.t1 : min(ctx, t0 + P);
   const bool uni = L::uniform(bshift);
 
-  const int tbl_entries = L::table_entries(sched ? max_piece(P, a.sched_q) : P, bshift);
+  const int tbl_entries = L::table_entries(a.sched_q > 0 ? max_piece(P, a.sched_q) : P, bshift);
   int* tbl = reinterpret_cast<int*>(smem);
   int* idslot = reinterpret_cast<int*>(smem + round16(tbl_entries * 4)) + w * L::kWaveWords;
   uint32_t* pbuf = reinterpret_cast<uint32_t*>(idslot + 128);
@@ -1237,8 +1325,8 @@ pkv_status launch_split(const DecodeArgs& a, hipStream_t st) {
   const int lds = L::bytes(L::table_entries(piece, a.block_shift));
   // shared-prefix decode: the leading slots belong to the shared pass
   dim3 grid(a.num_kv_heads, a.num_seqs, a.num_splits - a.sh.prefix_slots);
-  if (a.sched_q > 0) {
-    // pieces: at most num_splits per sequence
+  if (a.sched_q > 0 || a.sched_lpt) {
+    // pieces: at most num_splits per sequence (one in longest-first order)
     const int planes = a.num_seqs * a.num_splits;
     const int y = planes < kRowGridZ ? planes : kRowGridZ;
     grid = dim3(a.num_kv_heads, y, (planes + y - 1) / y);

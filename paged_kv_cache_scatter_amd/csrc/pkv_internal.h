@@ -89,7 +89,12 @@ struct DecodeArgs {
   // Each workgroup derives its piece from context_lens by a workgroup scan.
   int32_t sched_q;       // small piece (tokens); partition and sched_q are powers of two
   int32_t sched_align;   // piece starts are multiples of it (a power of two)
+  // Longest-first order for single-piece plans (at most kSchedMaxSeqs
+  // sequences): the grid's (y, z) plane enumerates the sequences by length
+  // class, longest class first (kLenClasses classes of the length range).
+  int32_t sched_lpt;
 };
+constexpr int kLenClasses = 4;
 constexpr int kSchedMaxSeqs = 1024;   // 4 sequences per thread of the scan
 
 // Pieces of a context of L tokens under the piece schedule (P large, Q small
