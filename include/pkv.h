@@ -132,19 +132,25 @@ pkv_status pkv_write(const void* k, const void* v, const int32_t* slot_mapping,
  *
  * Sequences are cut into pieces of `partition` tokens (a multiple of the
  * block size; 0 picks one from the sizes, see pkv_decode_partition). With at
- * most 1024 sequences each context is cut into full pieces of `partition`
- * tokens, then full pieces of half that, then its rest, and the launch runs
- * all large pieces first, then the small ones, then the rests (equal pieces
- * keep every workgroup stream of the GPU equally loaded and the last pieces
- * short). Each piece of a sequence with more than one yields a partial
+ * most 1024 sequences and a power-of-two partition the cut is finer: each
+ * context gets full pieces of `partition` tokens; a rest shorter than a
+ * quarter of it joins the last full piece, a longer one becomes one or two
+ * near-equal tail pieces of at most about half a partition; the launch runs
+ * all full pieces first, then the tail pieces, longer ones first
+ * (near-equal pieces keep every workgroup stream of the GPU equally loaded
+ * and the last pieces short). Each piece of a sequence with more than one yields a partial
  * (running max m in log2 units, exp-sum l, unnormalised o) in `workspace`;
  * the last workgroup of a (sequence, KV head) to finish merges them in the
- * same launch, counted by one int32 per (sequence, KV head) at the end of
- * the workspace. Sequences with a single piece are written directly.
+ * same launch, counted by one int32 per (sequence, KV head) in a fixed
+ * 256 KiB area at the start of the workspace (with more than 65536 such
+ * pairs a second kernel merges instead). Sequences with a single piece are
+ * written directly.
  * workspace (device) must hold pkv_decode_workspace_bytes(...) bytes; it may
- * be NULL when that is 0. Its counter words must be zero before the first
- * call that uses it (a zero-filled buffer); every call leaves them zero.
- * Calls that share a workspace must not overlap (run them in stream order).
+ * be NULL when that is 0. Its first 256 KiB must be zero before the first
+ * call that uses it (a zero-filled buffer); every call leaves them zero and
+ * writes partials only after them, so one buffer of the largest size serves
+ * calls of any size. Calls that share a workspace must not overlap (run
+ * them in stream order).
  *
  * context_lens[s] is clamped to [0, min(max_context_len,
  * max_blocks_per_seq * block_size)]; a sequence of length 0 gets zeros.
@@ -267,8 +273,9 @@ pkv_status pkv_decode_step_partials(const void* q, const void* k_new, const void
  *   are not attended). partition: tokens per tail split (0 = auto from
  *   max_tail_len), as in pkv_decode.
  * workspace: pkv_decode_shared_workspace_bytes(...) bytes (device, 16-byte
- *   aligned); 0 when no shared pass and no split is needed. Its counter words
- *   (at the end) must be zero before the first call, as for pkv_decode; the
+ *   aligned); 0 when no shared pass and no split is needed. Its counter
+ *   area (the first 256 KiB) must be zero before the first call, as for
+ *   pkv_decode; the
  *   tail launch merges the shared and tail partials, so a call is two launches
  *   (shared pass, tails + merge).
  * With num_groups == 0, max_prefix_len < block_size, or a shape the shared

@@ -17,6 +17,11 @@ thread_local char g_err[512] = "";
 
 constexpr int kMaxPartition = 8192;   // tokens per split (bounds the LDS table slice)
 constexpr int kMaxSplits = 4096;      // splits per sequence (bounds the merge kernel's LDS)
+// Merge counters: a fixed area at the start of every workspace, so that calls
+// of any size sharing one buffer never write partials where another counts.
+// Launches with more (sequence, KV head) pairs merge in a second kernel.
+constexpr size_t kMergeCounters = 65536;
+constexpr size_t kCounterBytes = kMergeCounters * sizeof(int32_t);   // 256 KiB
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 int ilog2(int x) {
@@ -61,21 +66,20 @@ struct DecodePlan {
   int sched_q = 0;      // small piece of the piece schedule (0: plain split grid)
   int sched_align = 0;
   bool sched_lpt = false;   // one piece per sequence, longest-first
-  size_t ws_ml_bytes = 0;
-  size_t ws_cnt_offset = 0;   // merge counters [S, Hkv] int32, after the partials
+  size_t ws_ml_offset = 0;   // partial (m, l) pairs, after the counter area
+  size_t ws_o_offset = 0;    // partial o rows
   size_t ws_bytes = 0;
 };
 
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-// Partials [S, Hq, J] (m, l) and o, then the merge counters.
+// The merge counter area, then partials [S, Hq, J] (m, l), then o.
 void plan_workspace(int32_t num_seqs, int32_t num_q_heads, const pkv_pool_desc* pool, int J,
                     DecodePlan* plan) {
   const size_t rows = (size_t)num_seqs * num_q_heads * J;
-  plan->ws_ml_bytes = round256(rows * 2 * sizeof(float));
-  plan->ws_cnt_offset = round256(plan->ws_ml_bytes + rows * (size_t)pool->head_dim * sizeof(float));
-  plan->ws_bytes = plan->ws_cnt_offset +
-                   round256((size_t)num_seqs * pool->num_kv_heads * sizeof(int32_t));
+  plan->ws_ml_offset = kCounterBytes;
+  plan->ws_o_offset = plan->ws_ml_offset + round256(rows * 2 * sizeof(float));
+  plan->ws_bytes = plan->ws_o_offset + round256(rows * (size_t)pool->head_dim * sizeof(float));
 }
 
 int align_tokens(const pkv_pool_desc* pool) {
@@ -171,7 +175,7 @@ pkv_status plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks
   }
   // single-piece plans: the sequences in longest-first order
   plan->sched_lpt = plan->splits == 1 && allow_sched && num_seqs <= kSchedMaxSeqs;
-  plan->ws_ml_bytes = plan->ws_cnt_offset = plan->ws_bytes = 0;
+  plan->ws_ml_offset = plan->ws_o_offset = plan->ws_bytes = 0;
   if (plan->splits > 1) plan_workspace(num_seqs, num_q_heads, pool, plan->splits, plan);
   return PKV_OK;
 }
@@ -291,10 +295,9 @@ pkv_status decode_impl(Phase phase, const void* q, int32_t num_seqs, int32_t num
   a.tables = block_tables;
   a.ctx_lens = context_lens;
   a.out = out;
-  a.ws_ml = plan.ws_bytes ? reinterpret_cast<float*>(workspace) : nullptr;
-  a.ws_o = plan.ws_bytes
-               ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + plan.ws_ml_bytes)
-               : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  a.ws_ml = plan.ws_bytes ? reinterpret_cast<float*>(ws + plan.ws_ml_offset) : nullptr;
+  a.ws_o = plan.ws_bytes ? reinterpret_cast<float*>(ws + plan.ws_o_offset) : nullptr;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = pool->num_kv_heads;
@@ -313,10 +316,11 @@ pkv_status decode_impl(Phase phase, const void* q, int32_t num_seqs, int32_t num
   a.k_new = k_new;
   a.v_new = v_new;
   a.sh = sd;
-  // One launch merges its own partials unless the caller runs the phases apart.
-  a.counters = (phase == Phase::kBoth && plan.ws_bytes)
-                   ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.ws_cnt_offset)
-                   : nullptr;
+  // One launch merges its own partials unless the caller runs the phases
+  // apart or there are more (sequence, KV head) pairs than counters.
+  const bool in_launch = phase == Phase::kBoth && plan.ws_bytes &&
+                         (size_t)num_seqs * pool->num_kv_heads <= kMergeCounters;
+  a.counters = in_launch ? reinterpret_cast<int32_t*>(ws) : nullptr;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (sd.group_start && phase != Phase::kReduce) {
     PrefillArgs p{};
@@ -346,7 +350,7 @@ pkv_status decode_impl(Phase phase, const void* q, int32_t num_seqs, int32_t num
     st = launch_decode_partials(a, pool->dtype, pool->head_dim, plan.rep, s);
     if (st != PKV_OK) return st;
   }
-  if (phase == Phase::kReduce) {
+  if (phase == Phase::kReduce || (phase == Phase::kBoth && plan.ws_bytes && !in_launch)) {
     st = launch_decode_reduce(a, pool->dtype, pool->head_dim, s);
     if (st != PKV_OK) return st;
   }

@@ -15,6 +15,7 @@ from paged_kv_cache_scatter_amd.sched import SCHED_EXPORTS
 
 INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
 HEADER = os.path.join(INCLUDE, "pkv.h")
+COUNTER_AREA = 65536 * 4   # merge counters at the start of every decode workspace
 
 
 @pytest.fixture(scope="module")
@@ -87,11 +88,11 @@ def test_workspace_bytes(lib):
     d = _desc(nb=32769, bs=16, hkv=8, hd=128)
     # 64 sequences x 64 heads x 10 partial slots: a context of up to 8192
     # tokens has at most 8 pieces of 1024 tokens and 2 tail pieces of at most
-    # 512 (slots: 8192 / 1024 + ceil(1023 / 512)); (m, l) then o[128], then
-    # one merge counter per (sequence, KV head), each part 256-byte aligned
+    # 512 (slots: 8192 / 1024 + ceil(1023 / 512)); the fixed merge counter
+    # area (65536 int32), then (m, l), then o[128], each part 256-byte aligned
     rows = 64 * 64 * 10
     assert lib.pkv_decode_workspace_bytes(64, 64, 8192, 1024, ctypes.byref(d)) == \
-        rows * 2 * 4 + rows * 128 * 4 + 64 * 8 * 4
+        COUNTER_AREA + rows * 2 * 4 + rows * 128 * 4
     assert lib.pkv_decode_workspace_bytes(64, 64, 1024, 1024, ctypes.byref(d)) == 0
     p = lib.pkv_decode_partition(64, 8192, ctypes.byref(d))
     assert p > 0 and p % 32 == 0 and p % 16 == 0
@@ -145,8 +146,7 @@ def test_shared_prefix_plan(lib):
     # tiles (64 members x 8 heads / 128 rows) = 32 units, so 16 key splits of
     # 128 tokens for about two workgroups per CU
     rows = 64 * 64 * (16 + 2)
-    counters = 64 * 8 * 4
-    assert _shared_ws(lib, d) == rows * 2 * 4 + rows * 128 * 4 + counters
+    assert _shared_ws(lib, d) == COUNTER_AREA + rows * 2 * 4 + rows * 128 * 4
     # no groups, a prompt shorter than a block, an uncompiled head size: plain decode
     plain = lib.pkv_decode_workspace_bytes(64, 64, 4096, 1024, ctypes.byref(d))
     assert _shared_ws(lib, d, G=0) == plain
@@ -155,7 +155,7 @@ def test_shared_prefix_plan(lib):
     assert _shared_ws(lib, d32) == lib.pkv_decode_workspace_bytes(64, 64, 4096, 1024,
                                                                   ctypes.byref(d32))
     # the tail partition follows max_tail_len; < 0 means max_context_len
-    assert _shared_ws(lib, d, mt=-1) == 64 * 64 * (16 + 4) * (2 + 128) * 4 + counters
+    assert _shared_ws(lib, d, mt=-1) == COUNTER_AREA + 64 * 64 * (16 + 4) * (2 + 128) * 4
     # inconsistent sizes give 0 bytes
     for kw in (dict(mp=5000), dict(G=65), dict(mg=0), dict(mg=65), dict(mt=5000), dict(G=-1)):
         assert _shared_ws(lib, d, **kw) == 0, kw

@@ -129,6 +129,27 @@ def test_step_tile_aligned_lengths():
         check_close(oracle.storage_to_f64(out, "bf16"), _ref_step(b), "bf16")
 
 
+def test_step_piece_boundaries():
+    """The fused step on the piece schedule: the new token is written by the
+    piece that ends the context, be it a full piece, a full piece with a short
+    rest joined to it, or a tail piece."""
+    lens = [0, 1, 100, 200, 255, 256, 257, 319, 320, 351, 352, 383, 384, 385, 511, 512, 513,
+            1088, 1224, 2047, 2048]
+    need = sum(-(-L // 16) for L in lens)
+    perm = (np.random.default_rng(91).permutation(need) + 1).tolist()
+    tabs, k = [], 0
+    for L in lens:
+        n = -(-L // 16)
+        tabs.append(perm[k:k + n])
+        k += n
+    wl = make_custom(tabs, lens, dtype="bf16", num_q_heads=16, num_kv_heads=2, head_dim=128,
+                     block_size=16, num_blocks=need + 1, seed=92)
+    for part in (256, 64):
+        b, out = _compare(wl, part)
+        assert not out[0].any()
+        check_close(oracle.storage_to_f64(out, "bf16"), _ref_step(b), "bf16", f"partition {part}")
+
+
 def test_step_invalid_block_for_new_token():
     """The new token's table entry is out of range: nothing is written and the
     token is left out, as with a skipped slot."""
