@@ -19,7 +19,10 @@ input rotation is needed.
 Prints one JSON line: whole-step KV-read GB/s (`value`), the roofline of the
 dominant kernel (the decode kernel: the step's only launch, so its mean
 duration is the step time between HIP events around the timed loop), and the
-CPU oracle timed on a bounded sample on the host.
+CPU oracle timed on a bounded sample on the host. Configs 3 and 4 are timed
+decode-only over rotating block sets, launched from Python and replayed from
+one captured HIP graph; the graph figure is the GPU's when a call is shorter
+than the binding's host-side time per call.
 """
 
 from __future__ import annotations
@@ -183,23 +186,57 @@ def time_decode_rotating(cfg: int, calls_per_set: int = 10):
         pkv.decode(q, k_pool, v_pool, tb, ctx, wl.scale, max_ctx, out=out, partition=part,
                    workspace=ws)
 
-    for r in range(sets * 2):
+    for r in range(max(sets * 2, 200)):
         call(tables[r % sets])
     torch.cuda.synchronize()
     n = sets * calls_per_set
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
     e0.record()
     for r in range(n):
         call(tables[r % sets])
     e1.record()
+    host_us = (time.perf_counter() - t0) / n * 1e6
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
+    eager_out = out.clone()
+    # The same n calls captured in one HIP graph: replays issue no host work
+    # per call, so a call shorter than the binding's host time is timed by the
+    # GPU alone. Every replay must reproduce the eager bits.
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(tables[0])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for r in range(n):
+            call(tables[r % sets])
+    for _ in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out, eager_out):
+            raise SystemExit(f"config {cfg}: graph replay differs from the eager calls")
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_graph = e0.elapsed_time(e1) / (reps * n)
+    if not torch.equal(out, eager_out):
+        raise SystemExit(f"config {cfg}: graph replay differs from the eager calls")
     kvb = wl.kv_bytes_per_call()
     return {"workload": workload_label(wl), "partition": part, "rotating_sets": sets,
             "us_per_call": round(ms * 1e3, 2), "kv_bytes": kvb,
             "kv_read_GBps": round(kvb / (ms * 1e-3) / 1e9, 1),
             "pct_hbm_peak": round(100 * kvb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
-            "seq_steps_per_s": round(wl.num_seqs / (ms * 1e-3), 1)}
+            "seq_steps_per_s": round(wl.num_seqs / (ms * 1e-3), 1),
+            "host_issue_us_per_call": round(host_us, 2),
+            "graph_us_per_call": round(ms_graph * 1e3, 2),
+            "graph_kv_read_GBps": round(kvb / (ms_graph * 1e-3) / 1e9, 1),
+            "graph_pct_hbm_peak": round(100 * kvb / (ms_graph * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)}
 
 
 SHARED_WORKLOADS = {

@@ -221,9 +221,10 @@ def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     if out is None:
         out = torch.empty_like(q)
     _dev(out, "out", q.dtype, q.shape)
-    need = decode_workspace_bytes(S, Hq, max_context_len, k_pool, partition)
-    if workspace is None and need > 0:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:   # a passed workspace is size-checked by the library
+        need = decode_workspace_bytes(S, Hq, max_context_len, k_pool, partition)
+        if need > 0:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0
     if workspace is not None:
         _dev(workspace, "workspace", torch.uint8)
@@ -275,10 +276,11 @@ def decode_shared(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     if out is None:
         out = torch.empty_like(q)
     _dev(out, "out", q.dtype, q.shape)
-    need = decode_shared_workspace_bytes(S, Hq, max_context_len, G, max_group_size,
-                                         max_prefix_len, max_tail_len, k_pool, partition)
-    if workspace is None and need > 0:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:   # a passed workspace is size-checked by the library
+        need = decode_shared_workspace_bytes(S, Hq, max_context_len, G, max_group_size,
+                                             max_prefix_len, max_tail_len, k_pool, partition)
+        if need > 0:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0
     if workspace is not None:
         _dev(workspace, "workspace", torch.uint8)
@@ -314,9 +316,10 @@ def decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
     if out is None:
         out = torch.empty_like(q)
     _dev(out, "out", q.dtype, q.shape)
-    need = decode_workspace_bytes(S, Hq, max_context_len, k_pool, partition)
-    if workspace is None and need > 0:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:   # a passed workspace is size-checked by the library
+        need = decode_workspace_bytes(S, Hq, max_context_len, k_pool, partition)
+        if need > 0:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0
     if workspace is not None:
         _dev(workspace, "workspace", torch.uint8)
