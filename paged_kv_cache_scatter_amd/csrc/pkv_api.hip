@@ -66,6 +66,8 @@ struct DecodePlan {
   int sched_q = 0;      // small piece of the piece schedule (0: plain split grid)
   int sched_align = 0;
   bool sched_lpt = false;   // one piece per sequence, longest-first
+  int pair_rep = 0;         // > 0: KV heads read in pairs (real group size)
+  pkv_pool_desc view{};     // the pool as the kernels read it
   size_t ws_ml_offset = 0;   // partial (m, l) pairs, after the counter area
   size_t ws_o_offset = 0;    // partial o rows
   size_t ws_bytes = 0;
@@ -114,9 +116,20 @@ int auto_partition(int num_seqs, int max_ctx, const pkv_pool_desc* pool) {
   return part;
 }
 
+// Adjacent KV heads read as one: bf16 rows of 64 dims (128 bytes) pair into
+// 256-byte rows, a layout the pool already has ([.., Hkv, 64] is
+// [.., Hkv / 2, 128]), when there are at least four (sequence, KV head) pairs
+// per CU: pairing halves the workgroups. Measured on Llama-3.2-1B's shape:
+// 192 sequences (1536 pairs) 82.5 us paired against 98.4 us; 8 sequences of
+// 2048 tokens (64 pairs) 16.0 us against 14.8 us.
+bool pair_heads(const pkv_pool_desc* pool, int num_seqs, int rep) {
+  return pool->dtype == PKV_BF16 && pool->head_dim == 64 && pool->num_kv_heads % 2 == 0 &&
+         rep <= 4 && (double)num_seqs * pool->num_kv_heads >= 4.0 * kNumCUs;
+}
+
 pkv_status plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
                        int32_t max_ctx, int32_t partition, const pkv_pool_desc* pool,
-                       DecodePlan* plan, bool allow_sched = true) {
+                       DecodePlan* plan, bool allow_sched = true, bool allow_pair = true) {
   pkv_status st = check_pool(pool);
   if (st != PKV_OK) return st;
   if (num_seqs < 0 || num_q_heads < 1 || max_ctx < 0 || max_blocks < 1) {
@@ -140,9 +153,17 @@ pkv_status plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks
               "group 1..8)", pool->head_dim, rep);
     return PKV_ERR_UNSUPPORTED;
   }
-  const int align = align_tokens(pool);
+  plan->view = *pool;
+  plan->pair_rep = 0;
+  if (allow_pair && pair_heads(pool, num_seqs, rep)) {
+    plan->pair_rep = rep;
+    plan->view.num_kv_heads /= 2;
+    plan->view.head_dim *= 2;
+  }
+  const int align = align_tokens(&plan->view);
   int part = partition;
   if (part == 0) {
+    // from the real heads: a multiple of their (coarser) alignment
     part = auto_partition(num_seqs, max_ctx, pool);
   } else if (part < 0 || part % align != 0 || part > kMaxPartition) {
     set_error("partition %d must be a positive multiple of %d and at most %d", part, align,
@@ -155,7 +176,7 @@ pkv_status plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks
               num_seqs, splits, kMaxSplits);
     return PKV_ERR_UNSUPPORTED;
   }
-  plan->rep = rep;
+  plan->rep = plan->pair_rep ? 2 * rep : rep;
   plan->partition = part;
   plan->splits = splits;
   plan->sched_q = 0;
@@ -176,7 +197,7 @@ pkv_status plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks
   // single-piece plans: the sequences in longest-first order
   plan->sched_lpt = plan->splits == 1 && allow_sched && num_seqs <= kSchedMaxSeqs;
   plan->ws_ml_offset = plan->ws_o_offset = plan->ws_bytes = 0;
-  if (plan->splits > 1) plan_workspace(num_seqs, num_q_heads, pool, plan->splits, plan);
+  if (plan->splits > 1) plan_workspace(num_seqs, num_q_heads, &plan->view, plan->splits, plan);
   return PKV_OK;
 }
 
@@ -213,7 +234,7 @@ pkv_status plan_shared(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks
       !shared_pass_supported(pool->dtype, pool->head_dim, plan->rep))
     return PKV_OK;
   const int tail = in.max_tail < 0 ? max_ctx : in.max_tail;
-  st = plan_decode(num_seqs, num_q_heads, max_blocks, tail, partition, pool, plan, false);
+  st = plan_decode(num_seqs, num_q_heads, max_blocks, tail, partition, pool, plan, false, false);
   if (st != PKV_OK) return st;
   const int64_t align = std::max(kSharedAlign, bs);
   const int64_t row_tiles = ((int64_t)in.max_group * plan->rep + kSharedRows - 1) / kSharedRows;
@@ -300,11 +321,13 @@ pkv_status decode_impl(Phase phase, const void* q, int32_t num_seqs, int32_t num
   a.ws_o = plan.ws_bytes ? reinterpret_cast<float*>(ws + plan.ws_o_offset) : nullptr;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
-  a.num_kv_heads = pool->num_kv_heads;
+  const pkv_pool_desc& view = plan.view;   // paired heads: half the heads, twice the dims
+  a.num_kv_heads = view.num_kv_heads;
   a.num_blocks = pool->num_blocks;
   a.block_shift = ilog2(pool->block_size);
   a.max_blocks = max_blocks;
   a.max_ctx = max_ctx;
+  a.pair_rep = plan.pair_rep;
   a.partition = plan.partition;
   a.num_splits = plan.splits;
   a.sched_q = plan.sched_q;
@@ -319,7 +342,7 @@ pkv_status decode_impl(Phase phase, const void* q, int32_t num_seqs, int32_t num
   // One launch merges its own partials unless the caller runs the phases
   // apart or there are more (sequence, KV head) pairs than counters.
   const bool in_launch = phase == Phase::kBoth && plan.ws_bytes &&
-                         (size_t)num_seqs * pool->num_kv_heads <= kMergeCounters;
+                         (size_t)num_seqs * view.num_kv_heads <= kMergeCounters;
   a.counters = in_launch ? reinterpret_cast<int32_t*>(ws) : nullptr;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (sd.group_start && phase != Phase::kReduce) {
@@ -347,11 +370,11 @@ pkv_status decode_impl(Phase phase, const void* q, int32_t num_seqs, int32_t num
     if (st != PKV_OK) return st;
   }
   if (phase != Phase::kReduce) {
-    st = launch_decode_partials(a, pool->dtype, pool->head_dim, plan.rep, s);
+    st = launch_decode_partials(a, view.dtype, view.head_dim, plan.rep, s);
     if (st != PKV_OK) return st;
   }
   if (phase == Phase::kReduce || (phase == Phase::kBoth && plan.ws_bytes && !in_launch)) {
-    st = launch_decode_reduce(a, pool->dtype, pool->head_dim, s);
+    st = launch_decode_reduce(a, view.dtype, view.head_dim, s);
     if (st != PKV_OK) return st;
   }
   return PKV_OK;

@@ -323,7 +323,7 @@ __device__ __forceinline__ bool live(const SplitCtx& c, const TileIds<Geo<T, HD,
 }
 
 // Scores of the tile's K rows (log2 units), reduce-scattered to the lane's heads.
-template <typename T, int HD, int REP, bool MASKED>
+template <typename T, int HD, int REP, bool MASKED, int PR>
 __device__ __forceinline__ void tile_scores(
     const SplitCtx& c, int kc, const uint4 (&qr)[REP][Geo<T, HD, REP>::KCH],
     const uint4 (&kr)[Geo<T, HD, REP>::RK][Geo<T, HD, REP>::KCH],
@@ -338,7 +338,11 @@ __device__ __forceinline__ void tile_scores(
       acc[h] = 0.f;
       if (h < REP) {
 #pragma unroll
-        for (int i = 0; i < G::KCH; ++i) acc[h] = chunk_dot<T>(qr[h][i], kr[r][i], acc[h]);
+        for (int i = 0; i < G::KCH; ++i) {
+          // paired heads: chunk i lies in real head i's half of the row
+          if (PR == 0 || i == h / (PR > 0 ? PR : 1))
+            acc[h] = chunk_dot<T>(qr[h][i], kr[r][i], acc[h]);
+        }
       }
     }
     reduce_scatter<G::LPT_K, G::REPP, G::HPL>(acc, kc);
@@ -542,7 +546,7 @@ __device__ __forceinline__ void issue_tile(const SplitCtx& c, const Lanes& ln, i
           base + (G::RK * G::KCH + r) * 1024);
 }
 
-template <typename T, int HD, int REP, bool UNI>
+template <typename T, int HD, int REP, bool UNI, int PR>
 __device__ __forceinline__ void compute_tile(const SplitCtx& c, const Lanes& ln,
                                              WaveState<T, HD, REP>& st,
                                              const uint4 (&qr)[REP][Geo<T, HD, REP>::KCH], int tb,
@@ -563,9 +567,9 @@ __device__ __forceinline__ void compute_tile(const SplitCtx& c, const Lanes& ln,
   if (ti.masked) {
 #pragma unroll
     for (int r = 0; r < G::RK; ++r) kval[r] = live<T, HD, REP, UNI>(c, ti, tb, tb + r * G::TPW_K + ln.kg);
-    tile_scores<T, HD, REP, true>(c, ln.kc, qr, kr, kval, sc);
+    tile_scores<T, HD, REP, true, PR>(c, ln.kc, qr, kr, kval, sc);
   } else {
-    tile_scores<T, HD, REP, false>(c, ln.kc, qr, kr, kval, sc);
+    tile_scores<T, HD, REP, false, PR>(c, ln.kc, qr, kr, kval, sc);
   }
   const bool moved = tile_softmax<T, HD, REP>(st, sc, ln.kg, ln.hb, ln.dup0, pbuf, cbuf);
   tile_pv<T, HD, REP>(st, stage + G::VOFF, ln.hg, ln.dl, moved, pbuf, cbuf);
@@ -586,7 +590,7 @@ __device__ __forceinline__ void wait_tiles_after(int behind) {
 
 // The wave's tiles tb0, tb0 + kStep, ... below t1. Tiles stream into the wave's
 // STAGES-deep LDS ring, STAGES - 1 tiles ahead of the one being computed.
-template <typename T, int HD, int REP, bool UNI, int kStep>
+template <typename T, int HD, int REP, bool UNI, int kStep, int PR>
 __device__ __forceinline__ void wave_tiles(const SplitCtx& c, const Lanes& ln,
                                            WaveState<T, HD, REP>& st,
                                            const uint4 (&qr)[REP][Geo<T, HD, REP>::KCH], int tb0,
@@ -639,8 +643,8 @@ __device__ __forceinline__ void wave_tiles(const SplitCtx& c, const Lanes& ln,
     } else {
       wait_tiles_after<G::LOADS, S>(n - 1 - k);
     }
-    compute_tile<T, HD, REP, UNI>(c, ln, st, qr, tb0 + k * kStep, ti[0], ring + (k % S) * G::STAGE,
-                                  pbuf, cbuf);
+    compute_tile<T, HD, REP, UNI, PR>(c, ln, st, qr, tb0 + k * kStep, ti[0],
+                                      ring + (k % S) * G::STAGE, pbuf, cbuf);
 #pragma unroll
     for (int q = 0; q < S - 1; ++q) ti[q] = ti[q + 1];
   }
@@ -698,18 +702,19 @@ __device__ __forceinline__ float2 ld_agent2(const float* p) {
   return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
 }
 
-template <typename T, int HD, int REP>
+template <typename T, int HD, int REP, int PR>
 __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int hq0, int nps,
                                                int slot0, int nsplit, T* out, float* wl, int w,
                                                int lane) {
-  constexpr int DPT = HD >= 64 ? HD / 64 : 1;   // dims per lane
+  constexpr int QHD = PR ? HD / 2 : HD;          // dims of one query head's output
+  constexpr int DPT = QHD >= 64 ? QHD / 64 : 1;  // dims per lane
   const int n = nps + nsplit;
   const int J = a.num_splits;
   auto slot = [&](int i) { return i < nps ? i : slot0 + i - nps; };
   for (int h = w; h < REP; h += kWaves) {
     const size_t row0 = ((size_t)s * a.num_q_heads + hq0 + h) * J;
     const float* ml = a.ws_ml + row0 * 2;
-    const float* po = a.ws_o + row0 * HD;
+    const float* po = a.ws_o + row0 * HD + (PR ? h / (PR > 0 ? PR : 1) : 0) * QHD;
     float M = -INFINITY, Ls = 0.f, f = 0.f;
     if (n <= 64) {
       const float2 v = lane < n ? ld_agent2(ml + 2 * slot(lane)) : make_float2(-INFINITY, 0.f);
@@ -744,7 +749,7 @@ __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int h
 #pragma unroll
           for (int e = 0; e < DPT; ++e) {
             const int d = lane + 64 * e;
-            ov[k][e] = d < HD ? ld_agent(pk + d) : 0.f;
+            ov[k][e] = d < QHD ? ld_agent(pk + d) : 0.f;
           }
         }
 #pragma unroll
@@ -761,7 +766,7 @@ __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int h
 #pragma unroll
     for (int e = 0; e < DPT; ++e) {
       const int d = lane + 64 * e;
-      if (d < HD) out[h * HD + d] = from_f32<T>(Ls > 0.f ? acc[e] / Ls : 0.f);
+      if (d < QHD) out[h * QHD + d] = from_f32<T>(Ls > 0.f ? acc[e] / Ls : 0.f);
     }
   }
 }
@@ -980,11 +985,16 @@ __device__ __forceinline__ bool find_sequence_lpt(const DecodeArgs& a, int pid, 
   return pc.s >= 0;
 }
 
-template <typename T, int HD, int REP>
+template <typename T, int HD, int REP, int PR>
 __global__ void __launch_bounds__(kThreads)
 decode_partials_kernel(DecodeArgs a) {
   using G = Geo<T, HD, REP>;
   using L = Lds<T, HD, REP>;
+  // PR > 0: paired KV heads (see DecodeArgs::pair_rep); chunk i of a lane's
+  // K row then lies in real head i's half, and q / out rows have QHD dims
+  static_assert(PR == 0 || (REP == 2 * PR && G::KCH == 2 && G::LPT_K * 16 * 2 == G::ROWB),
+                "paired heads need two K chunks per lane, one in each half");
+  constexpr int QHD = PR ? HD / 2 : HD;
   extern __shared__ __align__(16) unsigned char smem[];
 
   // Splits are dispatched last-index first: the later splits exist only for
@@ -1053,15 +1063,15 @@ decode_partials_kernel(DecodeArgs a) {
     nsplit = (ctx + P - 1) / P;
   }
   const int hq0 = g * REP;
-  T* out = reinterpret_cast<T*>(a.out) + ((size_t)qrow * a.num_q_heads + hq0) * HD;
+  T* out = reinterpret_cast<T*>(a.out) + ((size_t)qrow * a.num_q_heads + hq0) * QHD;
 
   if (sched ? ctx == 0 : j >= nsplit) {
     if (j == 0 && nps == 0) {  // empty sequence: zeros
-      for (int i = tid; i < REP * HD; i += kThreads) out[i] = from_f32<T>(0.f);
+      for (int i = tid; i < REP * QHD; i += kThreads) out[i] = from_f32<T>(0.f);
     } else if (j == 0 && a.counters) {
       // context inside the shared prompt: only the shared pass's partials,
       // written by the previous launch
-      merge_partials<T, HD, REP>(a, s, hq0, nps, slot0, 0, out,
+      merge_partials<T, HD, REP, PR>(a, s, hq0, nps, slot0, 0, out,
                                  reinterpret_cast<float*>(smem) + w * 64, w, lane);
     }
     return;
@@ -1136,13 +1146,19 @@ decode_partials_kernel(DecodeArgs a) {
   ln.dl = lane % G::LPH;
   ln.hb = head_base<G::LPT_K, G::REPP, G::HPL>(ln.kc);
   ln.dup0 = (ln.kc & (G::DUP - 1)) == 0;
-  const T* qp = reinterpret_cast<const T*>(a.q) + ((size_t)qrow * a.num_q_heads + hq0) * HD;
+  const T* qp = reinterpret_cast<const T*>(a.q) + ((size_t)qrow * a.num_q_heads + hq0) * QHD;
   uint4 qr[REP][G::KCH];
 #pragma unroll
   for (int h = 0; h < REP; ++h)
 #pragma unroll
-    for (int i = 0; i < G::KCH; ++i)
-      qr[h][i] = *reinterpret_cast<const uint4*>(qp + h * HD + (ln.kc + i * G::LPT_K) * G::EPC);
+    for (int i = 0; i < G::KCH; ++i) {
+      if (PR == 0)
+        qr[h][i] = *reinterpret_cast<const uint4*>(qp + h * HD + (ln.kc + i * G::LPT_K) * G::EPC);
+      else   // only the chunk in the head's own half is used
+        qr[h][i] = i == h / (PR > 0 ? PR : 1)
+                       ? *reinterpret_cast<const uint4*>(qp + h * QHD + ln.kc * G::EPC)
+                       : make_uint4(0u, 0u, 0u, 0u);
+    }
 
   {
     const size_t head_off = (size_t)g * HD * G::ISZ;
@@ -1172,10 +1188,11 @@ decode_partials_kernel(DecodeArgs a) {
   const int tb0 = t0 + w * G::TILE;
   if (tb0 < t1) {
     if (uni)
-      wave_tiles<T, HD, REP, true, kStep>(c, ln, st, qr, tb0, false, pbuf, cbuf, idslot, ring);
+      wave_tiles<T, HD, REP, true, kStep, PR>(c, ln, st, qr, tb0, false, pbuf, cbuf, idslot,
+                                              ring);
     else
-      wave_tiles<T, HD, REP, false, kStep>(c, ln, st, qr, tb0, any_bad, pbuf, cbuf, idslot,
-                                            ring);
+      wave_tiles<T, HD, REP, false, kStep, PR>(c, ln, st, qr, tb0, any_bad, pbuf, cbuf, idslot,
+                                               ring);
   }
 
   // ---- per-wave totals, then merge the waves in LDS
@@ -1204,8 +1221,10 @@ decode_partials_kernel(DecodeArgs a) {
   __syncthreads();
 
   const int J = a.num_splits;
-  for (int idx = tid; idx < REP * HD; idx += kThreads) {
-    const int h = idx / HD, d = idx % HD;
+  for (int idx = tid; idx < REP * QHD; idx += kThreads) {
+    // d: dim of the (virtual) row; a paired head's own half only
+    const int h = idx / QHD, dq = idx % QHD;
+    const int d = PR ? dq + (h / (PR > 0 ? PR : 1)) * QHD : dq;
     float M = -INFINITY;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, merge[ww * L::kMergeFloats + h]);
@@ -1220,20 +1239,20 @@ decode_partials_kernel(DecodeArgs a) {
       }
     }
     if (nsplit == 1 && nps == 0) {
-      out[h * HD + d] = from_f32<T>(Ls > 0.f ? O / Ls : 0.f);
+      out[h * QHD + dq] = from_f32<T>(Ls > 0.f ? O / Ls : 0.f);
     } else {
       const size_t row = ((size_t)s * a.num_q_heads + hq0 + h) * J + slot0 + j;
       if (a.counters) {
         // read back in this launch by another workgroup, possibly on another
         // XCD: device-coherent stores, written through the XCD's L2
         st_agent(a.ws_o + row * HD + d, O);
-        if (d == 0) {
+        if (dq == 0) {
           st_agent(a.ws_ml + row * 2, M);
           st_agent(a.ws_ml + row * 2 + 1, Ls);
         }
       } else {
         a.ws_o[row * HD + d] = O;
-        if (d == 0) {
+        if (dq == 0) {
           a.ws_ml[row * 2] = M;
           a.ws_ml[row * 2 + 1] = Ls;
         }
@@ -1262,7 +1281,7 @@ decode_partials_kernel(DecodeArgs a) {
     __syncthreads();
     if (!*last) return;
   }
-  merge_partials<T, HD, REP>(a, s, hq0, nps, slot0, nsplit, out,
+  merge_partials<T, HD, REP, PR>(a, s, hq0, nps, slot0, nsplit, out,
                              reinterpret_cast<float*>(smem) + w * 64, w, lane);
 }
 
@@ -1308,9 +1327,12 @@ __global__ void __launch_bounds__(64) decode_reduce_kernel(DecodeArgs a, int hea
   }
   Ls = group_sum<64>(Ls);
   __syncthreads();
-  const float* po = a.ws_o + row0 * head_dim;
-  T* out = reinterpret_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + h) * head_dim;
-  for (int d = lane; d < head_dim; d += 64) {
+  // paired heads: virtual rows of head_dim, this head's half of them
+  const int qhd = a.pair_rep > 0 ? head_dim / 2 : head_dim;
+  const int half = a.pair_rep > 0 ? (h % (2 * a.pair_rep)) / a.pair_rep : 0;
+  const float* po = a.ws_o + row0 * head_dim + half * qhd;
+  T* out = reinterpret_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + h) * qhd;
+  for (int d = lane; d < qhd; d += 64) {
     float O = 0.f;
     for (int i = 0; i < n; ++i) O = fmaf(wts[i], po[(size_t)slot(i) * head_dim + d], O);
     out[d] = from_f32<T>(Ls > 0.f ? O / Ls : 0.f);
@@ -1318,7 +1340,7 @@ __global__ void __launch_bounds__(64) decode_reduce_kernel(DecodeArgs a, int hea
 }
 
 
-template <typename T, int HD, int REP>
+template <typename T, int HD, int REP, int PR = 0>
 pkv_status launch_split(const DecodeArgs& a, hipStream_t st) {
   using L = Lds<T, HD, REP>;
   const int piece = a.sched_q > 0 ? max_piece(a.partition, a.sched_q) : a.partition;
@@ -1334,7 +1356,7 @@ pkv_status launch_split(const DecodeArgs& a, hipStream_t st) {
     const int z = a.total_q < kRowGridZ ? a.total_q : kRowGridZ;
     grid = dim3(a.num_kv_heads, (a.total_q + z - 1) / z, z);
   }
-  hipLaunchKernelGGL((decode_partials_kernel<T, HD, REP>), grid, dim3(kThreads), lds, st, a);
+  hipLaunchKernelGGL((decode_partials_kernel<T, HD, REP, PR>), grid, dim3(kThreads), lds, st, a);
   return launch_status("decode_partials_kernel");
 }
 
@@ -1384,6 +1406,21 @@ bool decode_supported(int dtype, int head_dim, int rep) {
 
 pkv_status launch_decode_partials(const DecodeArgs& a, int dtype, int head_dim, int rep,
                                   hipStream_t st) {
+  if (a.pair_rep > 0) {
+    // paired bf16 heads of 64 dims: virtual heads of 128, groups of 2 * pair_rep
+    if (dtype == PKV_BF16 && head_dim == 128 && rep == 2 * a.pair_rep) {
+      switch (a.pair_rep) {
+        case 1: return launch_split<uint16_t, 128, 2, 1>(a, st);
+        case 2: return launch_split<uint16_t, 128, 4, 2>(a, st);
+        case 3: return launch_split<uint16_t, 128, 6, 3>(a, st);
+        case 4: return launch_split<uint16_t, 128, 8, 4>(a, st);
+        default: break;
+      }
+    }
+    set_error("paired heads: no kernel for dtype %d, virtual head_dim %d, group %d", dtype,
+              head_dim, rep);
+    return PKV_ERR_UNSUPPORTED;
+  }
   if (dtype == PKV_F32) return dispatch_hd<float>(a, head_dim, rep, st);
   return dispatch_hd<uint16_t>(a, head_dim, rep, st);
 }

@@ -93,6 +93,12 @@ struct DecodeArgs {
   // sequences): the grid's (y, z) plane enumerates the sequences by length
   // class, longest class first (kLenClasses classes of the length range).
   int32_t sched_lpt;
+  // Paired KV heads (> 0: the group size of the real heads): the pool is read
+  // as num_kv_heads virtual heads of two adjacent real heads each (rows of
+  // 2 * head_dim, the same bytes), a workgroup serving both groups' query
+  // heads. Each query head takes its dot products over its own head's half
+  // only; q and out keep the real head_dim, the workspace the virtual one.
+  int32_t pair_rep;
 };
 constexpr int kLenClasses = 4;
 constexpr int kSchedMaxSeqs = 1024;   // 4 sequences per thread of the scan

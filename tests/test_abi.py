@@ -174,3 +174,25 @@ def test_shared_prefix_argument_errors(lib):
     assert call(mg=0) == 3
     assert call(ws=None, wsb=0) == 5 and "workspace" in _err(lib)
     assert call(S=0, G=0, mg=0) == 0      # nothing to do
+
+
+def test_paired_heads_show_in_the_workspace(lib):
+    """bf16 pools of head_dim 64 with at least 1024 (sequence, KV head) pairs
+    are read two KV heads at a time: the partial o rows are 128 floats wide."""
+    def ws(S, hkv=2, hq=8, dtype=1, hd=64, part=32, max_ctx=100):
+        d = _desc(nb=4096, bs=16, hkv=hkv, hd=hd, dtype=dtype)
+        return lib.pkv_decode_workspace_bytes(S, hq, max_ctx, part, ctypes.byref(d))
+
+    def expect(S, hq, slots, width):
+        rows = S * hq * slots
+        return COUNTER_AREA + -(-rows * 8 // 256) * 256 + -(-rows * width * 4 // 256) * 256
+
+    # 100 tokens in pieces of 32: 3 full slots, then tail slots of at most
+    # half a piece rounded to the alignment -- 2 of 16 tokens for the 16-token
+    # alignment of 256-byte rows (paired bf16, fp32), 1 of 32 for 128-byte rows
+    assert ws(512) == expect(512, 8, 5, 128)
+    # 1022 pairs, fp32, odd KV heads, groups over 4: plain rows of 64
+    assert ws(511) == expect(511, 8, 4, 64)
+    assert ws(512, dtype=0) == expect(512, 8, 5, 64)
+    assert ws(1024, hkv=1, hq=4) == expect(1024, 4, 4, 64)
+    assert ws(512, hq=10) == expect(512, 10, 4, 64)
