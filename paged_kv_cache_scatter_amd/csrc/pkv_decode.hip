@@ -227,6 +227,24 @@ __device__ __forceinline__ float strided_reduce(float x) {
   return x;
 }
 
+// PV-stage lane layout: HG head sets of HPV heads, LPH lanes per set, each
+// lane DPL dims starting at dim0(hg, dl). Paired heads (PR > 0): twice the
+// sets, each holding heads of one real head only and only that head's half
+// of the (virtual) dims, so no lane accumulates dims it will not store.
+template <typename T, int HD, int REP, int PR>
+struct PvGeo {
+  using G = Geo<T, HD, REP>;
+  static constexpr int HG = PR ? 2 * G::HG : G::HG;
+  static constexpr int LPH = PR ? G::LPH / 2 : G::LPH;
+  static constexpr int HPV = PR ? REP / HG : G::HPV;
+  static constexpr int DPL = G::DPL;
+  static_assert(PR == 0 || (HG * HPV == REP && LPH * DPL == HD / 2 && HPV <= PR),
+                "paired PV layout: every head set within one half");
+  __device__ static int dim0(int hg, int dl) {
+    return (PR ? (hg * HPV / (PR > 0 ? PR : 1)) * (HD / 2) : 0) + dl * DPL;
+  }
+};
+
 template <typename T, int HD, int REP>
 struct WaveState {
   using G = Geo<T, HD, REP>;
@@ -428,20 +446,21 @@ __device__ __forceinline__ void lds_words(const uint32_t* p, uint32_t (&w)[N]) {
 
 // o[h][d] += sum_t p[t][h] * V[t][d] for the lane's DPL dims of HPV heads,
 // reading the tile's V rows (token-major, ROWB bytes each) from LDS.
-template <typename T, int HD, int REP>
+template <typename T, int HD, int REP, int PR>
 __device__ __forceinline__ void tile_pv(WaveState<T, HD, REP>& st, const unsigned char* vt,
-                                        int hg, int dl, bool rescale, const uint32_t* pbuf,
+                                        int hg, int d0, bool rescale, const uint32_t* pbuf,
                                         const float* cbuf) {
   using G = Geo<T, HD, REP>;
+  using PV = PvGeo<T, HD, REP, PR>;
   if (rescale) {
 #pragma unroll
-    for (int i = 0; i < G::HPV; ++i) {
-      const float cr = cbuf[hg * G::HPV + i];
+    for (int i = 0; i < PV::HPV; ++i) {
+      const float cr = cbuf[hg * PV::HPV + i];
 #pragma unroll
       for (int e = 0; e < G::DPL; ++e) st.o[i][e] *= cr;
     }
   }
-  const unsigned char* vl = vt + dl * G::DPL * G::ISZ;
+  const unsigned char* vl = vt + d0 * G::ISZ;
   if constexpr (G::ISZ == 2) {
     // bf16: two tokens at a time. Their probabilities are a packed bf16 pair
     // and their V values of one dimension are packed side by side, so one
@@ -449,16 +468,16 @@ __device__ __forceinline__ void tile_pv(WaveState<T, HD, REP>& st, const unsigne
     constexpr int W = G::DPL / 2;   // words of V per token and lane
 #pragma unroll
     for (int pp = 0; pp < G::TILE / 2; ++pp) {
-      uint32_t a[W], b[W], pr[G::HPV];
+      uint32_t a[W], b[W], pr[PV::HPV];
       lds_words<W, G::ROWB / 4>(reinterpret_cast<const uint32_t*>(vl + 2 * pp * G::ROWB), a);
       lds_words<W, G::ROWB / 4>(reinterpret_cast<const uint32_t*>(vl + (2 * pp + 1) * G::ROWB), b);
-      lds_words<G::HPV, G::PSTR>(pbuf + pp * G::PSTR + hg * G::HPV, pr);
+      lds_words<PV::HPV, G::PSTR>(pbuf + pp * G::PSTR + hg * PV::HPV, pr);
 #pragma unroll
       for (int q = 0; q < W; ++q) {
         const uint32_t lo = __builtin_amdgcn_perm(b[q], a[q], 0x05040100u);  // dim 2q
         const uint32_t hi = __builtin_amdgcn_perm(b[q], a[q], 0x07060302u);  // dim 2q+1
 #pragma unroll
-        for (int i = 0; i < G::HPV; ++i) {
+        for (int i = 0; i < PV::HPV; ++i) {
           st.o[i][2 * q] = dot2_bf16(pr[i], lo, st.o[i][2 * q]);
           st.o[i][2 * q + 1] = dot2_bf16(pr[i], hi, st.o[i][2 * q + 1]);
         }
@@ -468,12 +487,12 @@ __device__ __forceinline__ void tile_pv(WaveState<T, HD, REP>& st, const unsigne
     const float* pf = reinterpret_cast<const float*>(pbuf);
 #pragma unroll
     for (int t = 0; t < G::TILE; ++t) {
-      uint32_t v[G::DPL], pr[G::HPV];
+      uint32_t v[G::DPL], pr[PV::HPV];
       lds_words<G::DPL, G::ROWB / 4>(reinterpret_cast<const uint32_t*>(vl + t * G::ROWB), v);
-      lds_words<G::HPV, G::PSTR>(reinterpret_cast<const uint32_t*>(pf) + t * G::PSTR + hg * G::HPV,
-                                 pr);
+      lds_words<PV::HPV, G::PSTR>(
+          reinterpret_cast<const uint32_t*>(pf) + t * G::PSTR + hg * PV::HPV, pr);
 #pragma unroll
-      for (int i = 0; i < G::HPV; ++i)
+      for (int i = 0; i < PV::HPV; ++i)
 #pragma unroll
         for (int e = 0; e < G::DPL; ++e)
           st.o[i][e] = fmaf(__uint_as_float(pr[i]), __uint_as_float(v[e]), st.o[i][e]);
@@ -483,7 +502,7 @@ __device__ __forceinline__ void tile_pv(WaveState<T, HD, REP>& st, const unsigne
 
 // Lane layout and per-lane address offsets (the same for every split).
 struct Lanes {
-  int lane, kg, kc, vg, hb, hg, dl;
+  int lane, kg, kc, vg, hb, hg, vd0;   // vd0: first dim of the lane's PV share
   bool dup0;
   uint32_t kc16, vc16;   // lane's 16-byte chunk within a K / V row
   uint32_t koff, voff;   // lane's chunk within a row group: kg*rsb + kc*16, vg*rsb + vc*16
@@ -572,7 +591,7 @@ __device__ __forceinline__ void compute_tile(const SplitCtx& c, const Lanes& ln,
     tile_scores<T, HD, REP, false, PR>(c, ln.kc, qr, kr, kval, sc);
   }
   const bool moved = tile_softmax<T, HD, REP>(st, sc, ln.kg, ln.hb, ln.dup0, pbuf, cbuf);
-  tile_pv<T, HD, REP>(st, stage + G::VOFF, ln.hg, ln.dl, moved, pbuf, cbuf);
+  tile_pv<T, HD, REP, PR>(st, stage + G::VOFF, ln.hg, ln.vd0, moved, pbuf, cbuf);
 }
 
 template <int LOADS, int S>
@@ -1142,8 +1161,9 @@ decode_partials_kernel(DecodeArgs a) {
   ln.kc = lane % G::LPT_K;
   ln.vg = lane / G::LPT_V;
   const int vc = lane % G::LPT_V;
-  ln.hg = lane / G::LPH;
-  ln.dl = lane % G::LPH;
+  using PV = PvGeo<T, HD, REP, PR>;
+  ln.hg = lane / PV::LPH;
+  ln.vd0 = PV::dim0(ln.hg, lane % PV::LPH);
   ln.hb = head_base<G::LPT_K, G::REPP, G::HPL>(ln.kc);
   ln.dup0 = (ln.kc & (G::DUP - 1)) == 0;
   const T* qp = reinterpret_cast<const T*>(a.q) + ((size_t)qrow * a.num_q_heads + hq0) * QHD;
@@ -1211,11 +1231,11 @@ decode_partials_kernel(DecodeArgs a) {
     }
   }
 #pragma unroll
-  for (int i = 0; i < G::HPV; ++i) {
-    const int h = ln.hg * G::HPV + i;
+  for (int i = 0; i < PV::HPV; ++i) {
+    const int h = ln.hg * PV::HPV + i;
     if (h < REP) {
 #pragma unroll
-      for (int e = 0; e < G::DPL; ++e) mw[2 * REP + h * HD + ln.dl * G::DPL + e] = st.o[i][e];
+      for (int e = 0; e < G::DPL; ++e) mw[2 * REP + h * HD + ln.vd0 + e] = st.o[i][e];
     }
   }
   __syncthreads();
