@@ -461,7 +461,7 @@ def _counter_rows(run_dir: str, counter: str):
 
 
 def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes,
-                       kernel_key="decode_partials_kernel<unsigned short, 128, 8>"):
+                       kernel_key="decode_partials_kernel<unsigned short, 128, 8, 0>"):
     """HBM bytes per launch of the dominant kernel from four rocprofv3 --pmc runs
     (FETCH_SIZE and WRITE_SIZE in KiB per dispatch, of the kernel and of a plain
     copy of copy_bytes), each counter scaled by what it reads for the copy."""
