@@ -22,7 +22,10 @@ duration is the step time between HIP events around the timed loop), and the
 CPU oracle timed on a bounded sample on the host. Configs 3 and 4 are timed
 decode-only over rotating block sets, launched from Python and replayed from
 one captured HIP graph; the graph figure is the GPU's when a call is shorter
-than the binding's host-side time per call.
+than the binding's host-side time per call. Each leg also reports single
+launches after a 512 MiB cache-evicting write ("cold", percentiles), the
+decode-only configs the same block set back to back ("warm", cache-assisted),
+and the step the percentiles of its launches timed one by one.
 """
 
 from __future__ import annotations
@@ -148,8 +151,32 @@ def time_steps(step: Step, steps: int, warmup: int):
     for i in range(steps):
         step.run(ev_a[i], ev_b[i])
     torch.cuda.synchronize()
-    ms_bracketed = float(np.mean([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]))
-    return ms_step, ms_bracketed
+    each = np.array([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)])
+    return ms_step, float(each.mean()), percentiles_us(each)
+
+
+def percentiles_us(ms: np.ndarray) -> dict:
+    return {f"p{q}": round(float(np.percentile(ms, q)) * 1e3, 2) for q in (10, 50, 90)}
+
+
+COLD_FLUSH_BYTES = 512 << 20   # twice the 256 MB Infinity Cache, far above the L2s
+
+
+def time_cold(fn, reps: int = 20) -> dict:
+    """Single calls after a 512 MiB device write that evicts the caches: the
+    percentiles of the per-call times (events around each call only)."""
+    scratch = torch.empty(COLD_FLUSH_BYTES, dtype=torch.uint8, device=DEV)
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for i in range(reps):
+        scratch.fill_(i & 255)
+        ev_a[i].record()
+        fn()
+        ev_b[i].record()
+    torch.cuda.synchronize()
+    out = percentiles_us(np.array([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]))
+    del scratch
+    return out
 
 
 def time_decode_rotating(cfg: int, calls_per_set: int = 10):
@@ -219,6 +246,15 @@ def time_decode_rotating(cfg: int, calls_per_set: int = 10):
         if not torch.equal(out, eager_out):
             raise SystemExit(f"config {cfg}: graph replay differs from the eager calls")
     reps = 5
+    # warm: the same block set back to back (its K/V stay in the Infinity Cache
+    # when they fit: cache-assisted)
+    e0.record()
+    for _ in range(n):
+        call(tables[0])
+    e1.record()
+    torch.cuda.synchronize()
+    ms_warm = e0.elapsed_time(e1) / n
+    cold = time_cold(lambda: call(tables[0]))
     e0.record()
     for _ in range(reps):
         graph.replay()
@@ -236,7 +272,9 @@ def time_decode_rotating(cfg: int, calls_per_set: int = 10):
             "host_issue_us_per_call": round(host_us, 2),
             "graph_us_per_call": round(ms_graph * 1e3, 2),
             "graph_kv_read_GBps": round(kvb / (ms_graph * 1e-3) / 1e9, 1),
-            "graph_pct_hbm_peak": round(100 * kvb / (ms_graph * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)}
+            "graph_pct_hbm_peak": round(100 * kvb / (ms_graph * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+            "warm_us_per_call_cache_assisted": round(ms_warm * 1e3, 2),
+            "cold_us_per_call_percentiles": cold}
 
 
 SHARED_WORKLOADS = {
@@ -545,7 +583,8 @@ def main():
     step = Step(wl, args.partition)
     print(f"[bench] timing {args.steps} steps (warmup {args.warmup}), partition "
           f"{step.partition}", file=sys.stderr, flush=True)
-    ms_step, ms_bracketed = time_steps(step, args.steps, args.warmup)
+    ms_step, ms_bracketed, pct_launch = time_steps(step, args.steps, args.warmup)
+    cold = time_cold(step.run)
     kvb = wl.kv_bytes_per_call()
     gbs = kvb / (ms_step * 1e-3) / 1e9
     # the fused step is one launch of the decode kernel: its mean launch
@@ -582,13 +621,17 @@ def main():
                      "kernel_ms": round(ms_kernel, 5),
                      "kernel_ms_events_around_each_launch": round(ms_bracketed, 5),
                      "algorithmic_bytes_per_launch": kvb},
+        # spread of the launches timed one by one (events around each), and
+        # single launches after a cache-evicting write ("cold")
+        "launch_us_percentiles": pct_launch,
+        "cold_launch_us_percentiles": cold,
     }
     if not args.no_extra:
         del step
         torch.cuda.empty_cache()
         print("[bench] the same step with separate write launches", file=sys.stderr, flush=True)
         sep = Step(wl, args.partition, fused=False)
-        ms_sep, ms_sep_k = time_steps(sep, args.steps, args.warmup)
+        ms_sep, ms_sep_k, _ = time_steps(sep, args.steps, args.warmup)
         res["separate_write_step"] = {
             "step": "pkv_slot_mapping + pkv_write + pkv_decode (split decode and merge, "
                     "one launch)",
