@@ -25,7 +25,9 @@ one captured HIP graph; the graph figure is the GPU's when a call is shorter
 than the binding's host-side time per call. Each leg also reports single
 launches after a 512 MiB cache-evicting write ("cold", percentiles), the
 decode-only configs the same block set back to back ("warm", cache-assisted),
-and the step the percentiles of its launches timed one by one.
+and the step the percentiles of its launches timed one by one. The workload's
+chunked-prefill variant (pkv_prefill on the same pools) is timed too and
+reported against the dense bf16 matrix-core peak.
 """
 
 from __future__ import annotations
@@ -177,6 +179,52 @@ def time_cold(fn, reps: int = 20) -> dict:
     out = percentiles_us(np.array([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]))
     del scratch
     return out
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+
+
+def time_prefill(step: Step, calls: int = 10, warmup: int = 10):
+    """The workload's chunked-prefill variant on the step's pools: every
+    sequence's last ``prefill_chunk`` positions as causal query rows over its
+    whole context (pkv_prefill, matrix-core path), back to back between two
+    HIP events. Query values are N(0,1) drawn on the device (the timing does
+    not depend on them)."""
+    wl = step.wl
+    n, S = wl.prefill_chunk, wl.num_seqs
+    g = torch.Generator(device=DEV).manual_seed(55)
+    q = torch.randn((S * n, wl.num_q_heads, wl.head_dim), generator=g,
+                    device=DEV).to(step.q.dtype)
+    cu = torch.arange(0, S * n + 1, n, dtype=torch.int32, device=DEV)
+    out = torch.empty_like(q)
+
+    def call():
+        pkv.prefill(q, cu, step.k_pool, step.v_pool, step.tables, step.ctx, wl.scale, n,
+                    step.max_ctx, out=out)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(calls):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / calls
+    # row i of sequence s sits at position ctx - n + i and sees ctx - n + i + 1
+    # keys; QK and PV are 2 * hd flops per (query head, visible key) each
+    ctx = wl.context_lens.astype(np.int64)
+    assert (ctx >= n).all()
+    keys = int((n * ctx - n * (n - 1) // 2).sum())
+    flops = 4 * wl.head_dim * wl.num_q_heads * keys
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"workload": f"{workload_label(wl)}; chunked prefill of the last {n} positions "
+                        f"of every sequence ({S * n} query rows)",
+            "calls": calls, "ms_per_call": round(ms, 4), "flops_per_call": flops,
+            "roofline": {"bound": "mfma", "kernel": "prefill_mfma_kernel",
+                         "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}}
 
 
 def time_decode_rotating(cfg: int, calls_per_set: int = 10):
@@ -626,6 +674,9 @@ def main():
         "launch_us_percentiles": pct_launch,
         "cold_launch_us_percentiles": cold,
     }
+    if not args.no_extra and wl.prefill_chunk and wl.dtype == "bf16":
+        print("[bench] chunked prefill", file=sys.stderr, flush=True)
+        res["prefill"] = time_prefill(step)
     if not args.no_extra:
         del step
         torch.cuda.empty_cache()
