@@ -196,3 +196,8 @@ def test_paired_heads_show_in_the_workspace(lib):
     assert ws(512, dtype=0) == expect(512, 8, 5, 64)
     assert ws(1024, hkv=1, hq=4) == expect(1024, 4, 4, 64)
     assert ws(512, hq=10) == expect(512, 10, 4, 64)
+
+
+def test_too_many_sequences_is_refused(lib):
+    d = _desc()
+    assert _dec(lib, d, S=65536) == 4 and "65535" in _err(lib)

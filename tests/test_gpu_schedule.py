@@ -225,3 +225,45 @@ def test_merge_counter_area_limit():
         got = _decode(pc, 64, ws, q=pc.q[:n], tables=pc.tables[:n], ctx=pc.ctx[:n])
         check_close(out_f64(got, "bf16"), ref[:n], "bf16", f"{n} sequences x 64 KV heads")
         assert _counters_zero(ws, COUNTER_AREA)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_more_than_64_pieces_per_sequence(dtype):
+    """A 12,000-token context in 64-token pieces: 188 partials per (sequence,
+    head) on the piece schedule and 250 on the plain grid (partition 48), so
+    the merge walks its partials in several batches of 64 lanes, in the launch
+    and in the two-phase reduce kernel."""
+    lens = [12000, 4500, 70, 1, 0]
+    tabs, nb = _tables(lens, 16, np.random.default_rng(61))
+    wl = make_custom(tabs, lens, dtype=dtype, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                     block_size=16, num_blocks=nb, seed=62, name=f"long-{dtype}")
+    pc = PoolCase(wl)
+    ref = pc.ref_decode()
+    for part in (64, 48):
+        need, ws = _ws(pc, part)
+        both = to_host(_decode(pc, part, ws))
+        check_close(oracle.storage_to_f64(both, dtype), ref, dtype, f"partition {part}")
+        assert _counters_zero(ws, need)
+        out = torch.empty_like(pc.q)
+        for ph in ("partials", "reduce"):
+            _decode(pc, part, ws, phase=ph, out=out)
+        assert np.array_equal(bits(to_host(out)), bits(both)), part
+
+
+def test_most_sequences_the_grid_takes():
+    """65,535 sequences (the most a launch takes): one piece each in index
+    order, and pieces of 32 tokens merged in the launch (65,535 counters)."""
+    rng = np.random.default_rng(71)
+    S = 65535
+    lens = rng.integers(0, 81, size=S)
+    tabs, nb = _tables(lens, 16, rng)
+    wl = make_custom(tabs, lens, dtype="bf16", num_q_heads=2, num_kv_heads=1, head_dim=64,
+                     block_size=16, num_blocks=nb, seed=72, name="most-sequences")
+    pc = PoolCase(wl)
+    note("oracle over 65,535 sequences (about 15 s)")
+    ref = pc.ref_decode()
+    for part in (0, 32):
+        need, ws = _ws(pc, part)
+        got = out_f64(_decode(pc, part, ws), "bf16")
+        check_close(got, ref, "bf16", f"{S} sequences, partition {part}")
+        assert _counters_zero(ws, need)
