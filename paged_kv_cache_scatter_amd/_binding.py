@@ -207,7 +207,11 @@ def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     ``max_context_len`` is a host-side bound on ``context_lens`` (the library
     never reads device memory on the host). ``workspace`` is a uint8 device
     tensor of at least ``decode_workspace_bytes(...)`` bytes (allocated here
-    if omitted and needed). ``phase``: "both", "partials" or "reduce".
+    if omitted and needed). A passed workspace must be zero-filled before its
+    first use (``torch.zeros``, not ``torch.empty``): its first 256 KiB count
+    the pieces merged in the launch, and every call leaves them zero, so one
+    buffer serves calls of any size in stream order. ``phase``: "both",
+    "partials" or "reduce".
     """
     desc = _check_pools(k_pool, v_pool)
     _dev(q, "q", k_pool.dtype)
@@ -259,7 +263,9 @@ def decode_shared(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     blocks of their tables. ``group_start`` int32 [G+1] (members of group i are
     sequences group_start[i] .. group_start[i+1]-1), ``prefix_lens`` int32 [G]
     (shared tokens of each group). The ``max_*`` arguments are host-side bounds
-    (``max_tail_len`` < 0: ``max_context_len``). Same result as ``decode``."""
+    (``max_tail_len`` < 0: ``max_context_len``). ``workspace``: at least
+    ``decode_shared_workspace_bytes(...)`` bytes, zero-filled before its first
+    use as for ``decode``. Same result as ``decode``."""
     desc = _check_pools(k_pool, v_pool)
     _dev(q, "q", k_pool.dtype)
     _need(q.dim() == 3 and q.shape[2] == desc.head_dim, "q must be [S, Hq, head_dim]")
@@ -300,7 +306,8 @@ def decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                 workspace: torch.Tensor | None = None, phase: str = "both") -> torch.Tensor:
     """Decode step with the KV write fused in: k_new / v_new [S, Hkv, hd] are the
     new token of each sequence (position context_lens - 1); they are written into
-    their slots and attended. ``phase``: "both", "partials" (then call
+    their slots and attended. ``workspace`` as for ``decode`` (zero-filled
+    before its first use). ``phase``: "both", "partials" (then call
     ``decode(..., phase="reduce")`` with the same arguments) or "reduce"."""
     desc = _check_pools(k_pool, v_pool)
     _dev(q, "q", k_pool.dtype)
