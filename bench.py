@@ -457,7 +457,7 @@ def time_layer_graph(cfg: int, layers: int = 16, steps: int = 20):
     ms_graph = timed(st.replay)
     kvb = wl.kv_bytes_per_call() * L
     return {"workload": workload_label(wl) + f", {L} layers", "partition": st.partition,
-            "launches_per_step": 2 * L, "eager_us": round(ms_eager * 1e3, 2),
+            "launches_per_step": L, "eager_us": round(ms_eager * 1e3, 2),
             "graph_us": round(ms_graph * 1e3, 2), "speedup": round(ms_eager / ms_graph, 3),
             "graph_us_per_layer": round(ms_graph * 1e3 / L, 2),
             "kv_bytes_per_step": kvb, "graph_GBps": round(kvb / (ms_graph * 1e-3) / 1e9, 1)}
