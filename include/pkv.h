@@ -132,7 +132,9 @@ pkv_status pkv_write(const void* k, const void* v, const int32_t* slot_mapping,
  *
  * Sequences are cut into pieces of `partition` tokens (a multiple of the
  * block size; 0 picks one from the sizes, see pkv_decode_partition). With at
- * most 1024 sequences and a power-of-two partition the cut is finer: each
+ * most 1024 sequences, a power-of-two partition and pieces of at least
+ * 128 KiB of K and V (smaller ones finish before a schedule pays) the cut is
+ * finer: each
  * context gets full pieces of `partition` tokens; a rest shorter than a
  * quarter of it joins the last full piece, a longer one becomes one or two
  * near-equal tail pieces of at most about half a partition; the launch runs

@@ -187,13 +187,12 @@ def test_paired_heads_show_in_the_workspace(lib):
         rows = S * hq * slots
         return COUNTER_AREA + -(-rows * 8 // 256) * 256 + -(-rows * width * 4 // 256) * 256
 
-    # 100 tokens in pieces of 32: 3 full slots, then tail slots of at most
-    # half a piece rounded to the alignment -- 2 of 16 tokens for the 16-token
-    # alignment of 256-byte rows (paired bf16, fp32), 1 of 32 for 128-byte rows
-    assert ws(512) == expect(512, 8, 5, 128)
+    # 100 tokens in pieces of 32 (at most 32 KiB of K/V, too little to be worth
+    # the piece schedule's lookup): the plain grid's 4 slots
+    assert ws(512) == expect(512, 8, 4, 128)
     # 1022 pairs, fp32, odd KV heads, groups over 4: plain rows of 64
     assert ws(511) == expect(511, 8, 4, 64)
-    assert ws(512, dtype=0) == expect(512, 8, 5, 64)
+    assert ws(512, dtype=0) == expect(512, 8, 4, 64)
     assert ws(1024, hkv=1, hq=4) == expect(1024, 4, 4, 64)
     assert ws(512, hq=10) == expect(512, 10, 4, 64)
 
@@ -201,3 +200,18 @@ def test_paired_heads_show_in_the_workspace(lib):
 def test_too_many_sequences_is_refused(lib):
     d = _desc()
     assert _dec(lib, d, S=65536) == 4 and "65535" in _err(lib)
+
+
+def test_piece_schedule_needs_large_pieces(lib):
+    """The piece schedule (full pieces, then tail pieces: more slots than the
+    plain grid's ceil(max_context_len / partition)) is used only when a piece
+    carries at least 128 KiB of K and V."""
+    d = _desc(nb=32769, bs=16, hkv=8, hd=128)    # bf16 rows: 512 bytes of K+V per token
+
+    def slots(part, max_ctx=4000):
+        rows = 64 * 64
+        b = lib.pkv_decode_workspace_bytes(64, 64, max_ctx, part, ctypes.byref(d))
+        return (b - COUNTER_AREA) // (rows * (2 + 128) * 4)
+    assert slots(128) == -(-4000 // 128)           # 64 KiB pieces: plain grid
+    assert slots(256) == 4000 // 256 + 2           # 128 KiB pieces: schedule, up to two tails
+    assert slots(1024) == 4000 // 1024 + 2         # up to two tails of 512

@@ -21,7 +21,7 @@ S_PAIRED = 512     # x 2 KV heads = 1024 pairs: the smallest launch that pairs
 BF16_INF, BF16_NAN = 0x7F80, 0x7FC0
 
 
-def _workload(rep, seed, S=S_PAIRED, hi=120):
+def _workload(rep, seed, S=S_PAIRED, hi=600):
     rng = np.random.default_rng(seed)
     lens = rng.integers(1, hi + 1, size=S)
     lens[rng.choice(S, size=8, replace=False)] = 0
@@ -39,22 +39,22 @@ def _workload(rep, seed, S=S_PAIRED, hi=120):
 
 @pytest.mark.parametrize("rep", [1, 2, 3, 4])
 def test_paired_decode_matches_oracle(rep):
-    """One piece per sequence (automatic partition), pieces of 32 tokens on the
-    piece schedule, pieces of 48 on the plain grid, and the two phases called
-    apart (bit-equal to the one-launch call)."""
+    """One piece per sequence (automatic partition, longest first), pieces of
+    256 tokens on the piece schedule, pieces of 48 and 32 on the plain grid,
+    and the two phases called apart (bit-equal to the one-launch call)."""
     pc = PoolCase(_workload(rep, seed=60 + rep))
     ref = pc.ref_decode()
-    for part in (0, 32, 48):
+    for part in (0, 256, 48, 32):
         got = out_f64(pc.decode(partition=part), "bf16")
         check_close(got, ref, "bf16", f"rep {rep}, partition {part}")
-    both = to_host(pc.decode(partition=32))
+    both = to_host(pc.decode(partition=256))
     ws = torch.zeros(pkv.decode_workspace_bytes(pc.wl.num_seqs, pc.wl.num_q_heads, pc.max_ctx,
-                                                pc.k_pool, 32),
+                                                pc.k_pool, 256),
                      dtype=torch.uint8, device=pc.q.device)
     out = torch.empty_like(pc.q)
     for ph in ("partials", "reduce"):
         pkv.decode(pc.q, pc.k_pool, pc.v_pool, pc.tables, pc.ctx, pc.wl.scale, pc.max_ctx,
-                   out=out, partition=32, workspace=ws, phase=ph)
+                   out=out, partition=256, workspace=ws, phase=ph)
     torch.cuda.synchronize()
     assert np.array_equal(bits(to_host(out)), bits(both))
 
@@ -65,7 +65,7 @@ def test_paired_heads_stay_independent():
     kernel forms no product across heads and stores only a head's own half)."""
     pc = PoolCase(_workload(2, seed=71))
     wl = pc.wl
-    clean = [to_host(pc.decode(partition=p)) for p in (0, 32)]
+    clean = [to_host(pc.decode(partition=p)) for p in (0, 256)]
     L = int(wl.context_lens[0])
     assert L >= 2
     for pool, pos, val in ((pc.k_pool, 0, BF16_INF), (pc.v_pool, L - 1, BF16_NAN)):
@@ -73,7 +73,7 @@ def test_paired_heads_stay_independent():
         pool.view(torch.int16)[blk, pos % 16, 1, 5] = val
     torch.cuda.synchronize()
     note("decode with Inf / NaN in KV head 1 of sequence 0")
-    for p, ref in zip((0, 32), clean):
+    for p, ref in zip((0, 256), clean):
         got = to_host(pc.decode(partition=p))
         # query heads 0, 1 read KV head 0; 2, 3 read KV head 1
         assert np.array_equal(bits(got[:, :2]), bits(ref[:, :2])), p
@@ -92,10 +92,10 @@ def test_paired_fused_step():
     slots = pkv.slot_mapping(to_dev(tabs), to_dev(first), to_dev(cu), int(cu[-1]),
                              wl.block_size, wl.num_blocks)
     pkv.write(to_dev(wl.k_rows[srows]), to_dev(wl.v_rows[srows]), slots, a.k_pool, a.v_pool)
-    sep = to_host(a.decode(partition=32))
+    sep = to_host(a.decode(partition=256))
     note("paired fused step")
     fused = pkv.decode_step(b.q, to_dev(wl.k_rows[rows]), to_dev(wl.v_rows[rows]), b.k_pool,
-                            b.v_pool, b.tables, b.ctx, wl.scale, b.max_ctx, partition=32)
+                            b.v_pool, b.tables, b.ctx, wl.scale, b.max_ctx, partition=256)
     torch.cuda.synchronize()
     fused = to_host(fused)
     assert np.array_equal(bits(fused), bits(sep))

@@ -98,7 +98,8 @@ def test_piece_boundaries(dtype):
 
 def test_clamped_lengths_under_the_schedule():
     """Context lengths above max_context_len are clamped before the pieces
-    are counted (the slot count follows max_context_len)."""
+    are counted (the slot count follows max_context_len); 256-token pieces
+    (128 KiB of K and V) take the piece schedule, smaller ones the plain grid."""
     lens = [40, 700, 300, 5, 321, 0]
     tabs, nb = _tables(lens, 16, np.random.default_rng(13))
     wl = make_custom(tabs, lens, dtype="f32", num_q_heads=4, num_kv_heads=2, head_dim=64,
@@ -108,7 +109,7 @@ def test_clamped_lengths_under_the_schedule():
     cap = 320
     ref = oracle.decode(wl.q, kp, vp, wl.block_tables,
                         np.minimum(wl.context_lens, cap).astype(np.int32), wl.scale, "f32")
-    for part in (64, 128, 0):
+    for part in (256, 128, 64, 0):
         got = out_f64(_decode(pc, part, max_ctx=cap), "f32")
         check_close(got, ref, "f32", f"clamped, partition {part}")
 
@@ -126,16 +127,16 @@ def _many(S, lo, hi, seed, dtype="bf16", hd=64, hq=4, hkv=1):
 
 
 def test_schedule_and_plain_grid_at_the_sequence_limit():
-    """1025 sequences split into pieces run on the plain grid; their first
-    1024 run on the piece schedule. Both equal the oracle."""
-    pc = _many(SCHED_MAX_SEQS + 1, 1, 300, seed=21)
+    """1025 sequences split into 256-token pieces run on the plain grid; their
+    first 1024 run on the piece schedule. Both equal the oracle."""
+    pc = _many(SCHED_MAX_SEQS + 1, 1, 700, seed=21, hd=128)
     ref = pc.ref_decode()
-    got = out_f64(_decode(pc, 64), "bf16")
+    got = out_f64(_decode(pc, 256), "bf16")
     check_close(got, ref, "bf16", "1025 sequences, plain grid")
     S = SCHED_MAX_SEQS
-    need = pkv.decode_workspace_bytes(S, pc.wl.num_q_heads, pc.max_ctx, pc.k_pool, 64)
+    need = pkv.decode_workspace_bytes(S, pc.wl.num_q_heads, pc.max_ctx, pc.k_pool, 256)
     ws = torch.zeros(need, dtype=torch.uint8, device=pc.q.device)
-    part = _decode(pc, 64, ws, q=pc.q[:S], tables=pc.tables[:S], ctx=pc.ctx[:S])
+    part = _decode(pc, 256, ws, q=pc.q[:S], tables=pc.tables[:S], ctx=pc.ctx[:S])
     check_close(out_f64(part, "bf16"), ref[:S], "bf16", "1024 sequences, piece schedule")
     assert _counters_zero(ws, need)
 
@@ -144,7 +145,7 @@ def test_longest_first_order_changes_no_bit():
     """Single-piece launches: 1025 sequences run in index order, their first
     1024 in longest-first order; every output bit is the same, and both equal
     the oracle. Lengths fill all four length classes."""
-    pc = _many(SCHED_MAX_SEQS + 1, 1, 200, seed=22, hkv=2, hq=8)
+    pc = _many(SCHED_MAX_SEQS + 1, 1, 400, seed=22, hkv=2, hq=8)
     S = SCHED_MAX_SEQS
     assert pkv.decode_workspace_bytes(S + 1, 8, pc.max_ctx, pc.k_pool, 0) == 0   # one piece
     full = to_host(_decode(pc, 0))
@@ -229,17 +230,17 @@ def test_merge_counter_area_limit():
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_more_than_64_pieces_per_sequence(dtype):
-    """A 12,000-token context in 64-token pieces: 188 partials per (sequence,
-    head) on the piece schedule and 250 on the plain grid (partition 48), so
-    the merge walks its partials in several batches of 64 lanes, in the launch
-    and in the two-phase reduce kernel."""
-    lens = [12000, 4500, 70, 1, 0]
+    """Contexts of 20,000 and 12,000 tokens: 78 partials per (sequence, head)
+    on the piece schedule (256-token pieces), 313 and 417 on the plain grid
+    (64 and 48), so the merge walks its partials in several batches of 64
+    lanes, in the launch and in the two-phase reduce kernel."""
+    lens = [20000, 12000, 4500, 70, 1, 0]
     tabs, nb = _tables(lens, 16, np.random.default_rng(61))
     wl = make_custom(tabs, lens, dtype=dtype, num_q_heads=8, num_kv_heads=2, head_dim=128,
                      block_size=16, num_blocks=nb, seed=62, name=f"long-{dtype}")
     pc = PoolCase(wl)
     ref = pc.ref_decode()
-    for part in (64, 48):
+    for part in (256, 64, 48):
         need, ws = _ws(pc, part)
         both = to_host(_decode(pc, part, ws))
         check_close(oracle.storage_to_f64(both, dtype), ref, dtype, f"partition {part}")
