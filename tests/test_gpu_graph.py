@@ -20,6 +20,11 @@ BASES = {
     "llama-1b": lambda: make_shared([12], [0], ("uniform", 1, 600), dtype="bf16",
                                     num_q_heads=32, num_kv_heads=8, head_dim=64, seed=41,
                                     name="llama-3.2-1b-shape"),
+    # the same shape with 128 sequences: 1024 (sequence, KV head) pairs read
+    # two KV heads at a time, one piece per sequence in longest-first order
+    "llama-1b-paired": lambda: make_shared([128], [0], ("uniform", 1, 600), dtype="bf16",
+                                           num_q_heads=32, num_kv_heads=8, head_dim=64,
+                                           seed=43, name="llama-3.2-1b-shape-128"),
     # LLaMA-2-70B layer shape, 4 sequences
     "llama-70b": lambda: make_shared([4], [0], ("uniform", 1, 3000), dtype="bf16",
                                      num_q_heads=64, num_kv_heads=8, head_dim=128, seed=42,
@@ -51,7 +56,8 @@ def _ref_layer(pc):
     return oracle.decode(wl.q, kp, vp, wl.block_tables, wl.context_lens, wl.scale, wl.dtype)
 
 
-@pytest.mark.parametrize("name,L", [("llama-1b", 16), ("tiny", 3), ("llama-70b", 2)])
+@pytest.mark.parametrize("name,L", [("llama-1b", 16), ("tiny", 3), ("llama-70b", 2),
+                                    ("llama-1b-paired", 4)])
 def test_graph_replays_equal_eager(name, L):
     base, layers, cases, q, kn, vn, kp, vp = _layers(name, L, seed=L)
     kp0, vp0 = kp.clone(), vp.clone()
