@@ -598,7 +598,15 @@ def main():
     ap.add_argument("--layer-graph", nargs="+", type=int, metavar="CFG",
                     help="only time a 16-layer decode step of these configs, layer by layer "
                          "and replayed from one captured HIP graph")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the chunked-prefill leg, two calls after one warm-up (for "
+                         "counter runs)")
     args = ap.parse_args()
+    if args.prefill_only:
+        pkv.load()
+        step = Step(make_workload(args.config), args.partition)
+        print(json.dumps({"prefill": time_prefill(step, calls=2, warmup=1)}), flush=True)
+        return
     if args.layer_graph:
         pkv.load()
         for cfg in args.layer_graph:
