@@ -241,7 +241,7 @@ pkv_status plan_shared(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks
   }
   const int bs = pool->block_size;
   if (in.num_groups == 0 || in.max_prefix < bs ||
-      !shared_pass_supported(pool->dtype, pool->head_dim, plan->rep))
+      !shared_pass_supported(pool->dtype, pool->head_dim, num_q_heads / pool->num_kv_heads))
     return PKV_OK;
   const int tail = in.max_tail < 0 ? max_ctx : in.max_tail;
   st = plan_decode(num_seqs, num_q_heads, max_blocks, tail, partition, pool, plan, false, false);
