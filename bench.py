@@ -19,8 +19,9 @@ input rotation is needed.
 Prints one JSON line: whole-step KV-read GB/s (`value`), the roofline of the
 dominant kernel (the decode kernel: the step's only launch, so its mean
 duration is the step time between HIP events around the timed loop), and the
-CPU oracle timed on a bounded sample on the host. Configs 3 and 4 are timed
-decode-only over rotating block sets, launched from Python and replayed from
+CPU oracle timed on a bounded sample on the host. The two Llama-3.2-1B decode
+shapes (8 x 2048 tokens, and 192 sequences) are timed decode-only over rotating
+block sets, launched from Python and replayed from
 one captured HIP graph; the graph figure is the GPU's when a call is shorter
 than the binding's host-side time per call. Each leg also reports single
 launches after a 512 MiB cache-evicting write ("cold", percentiles), the
@@ -312,7 +313,8 @@ def time_decode_rotating(cfg: int, calls_per_set: int = 10):
     if not torch.equal(out, eager_out):
         raise SystemExit(f"config {cfg}: graph replay differs from the eager calls")
     kvb = wl.kv_bytes_per_call()
-    return {"workload": workload_label(wl), "partition": part, "rotating_sets": sets,
+    return {"name": wl.name, "workload": workload_label(wl), "partition": part,
+            "rotating_sets": sets,
             "us_per_call": round(ms * 1e3, 2), "kv_bytes": kvb,
             "kv_read_GBps": round(kvb / (ms * 1e-3) / 1e9, 1),
             "pct_hbm_peak": round(100 * kvb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
@@ -326,8 +328,9 @@ def time_decode_rotating(cfg: int, calls_per_set: int = 10):
 
 
 SHARED_WORKLOADS = {
-    # config 2: 30 sequences whose tables start with the same 32-token prompt
-    "config2": lambda: make_workload(2),
+    # 30 sequences at the SmolLM2-135M attention shape whose tables start with
+    # the same 32-token prompt
+    "smollm2-32": lambda: make_workload(2),
     # 30 users of a ~500-token system prompt at the SmolLM2-135M shape: its 31
     # full blocks (496 tokens) shared, own tails of 4 prompt tokens + 8..200
     "smollm2-500": lambda: make_shared([30], [496], ("uniform", 12, 204), dtype="f32",
@@ -586,7 +589,9 @@ def main():
     ap.add_argument("--config", type=int, default=5, choices=sorted(CONFIGS))
     ap.add_argument("--partition", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
-    ap.add_argument("--no-extra", action="store_true", help="skip configs 3 and 4")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other legs (separate-write step, chunked prefill, the "
+                         "Llama-3.2-1B decode shapes)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy (counter calibration)")
     ap.add_argument("--summarize-counters", nargs=4, metavar="DIR",
@@ -703,8 +708,9 @@ def main():
             if cfg == args.config:
                 continue
             print(f"[bench] rotating decode timing, config {cfg}", file=sys.stderr, flush=True)
-            extra[f"config{cfg}"] = time_decode_rotating(cfg)
-        res["other_configs_decode_only"] = extra
+            r = time_decode_rotating(cfg)
+            extra[r.pop("name")] = r
+        res["other_workloads_decode_only"] = extra
     if not args.no_cpu:
         print("[bench] CPU oracle sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl)

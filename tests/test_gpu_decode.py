@@ -221,9 +221,10 @@ def test_other_block_sizes(bs):
     check_close(out_f64(pc.decode(), "bf16"), pc.ref_decode(), "bf16", f"bs={bs}")
 
 
-def test_paired_step_then_decode_config4():
-    """The decode step of config 4: slot mapping and write of the new token at
-    position ctx-1, then attention over the whole context."""
+def test_step_write_then_decode_llama1b_192_sequences():
+    """The decode step of the 192-sequence Llama-3.2-1B workload: slot mapping
+    and write of the new token at position ctx-1, then attention over the
+    whole context."""
     wl = make_workload(4, num_seqs=32)
     pc = PoolCase(wl, exclude_last=True)
     tabs, first, cu, rows = wl.step_segments()

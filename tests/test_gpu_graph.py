@@ -29,7 +29,7 @@ BASES = {
     "llama-70b": lambda: make_shared([4], [0], ("uniform", 1, 3000), dtype="bf16",
                                      num_q_heads=64, num_kv_heads=8, head_dim=128, seed=42,
                                      name="llama-2-70b-layer-shape"),
-    # the toy fp32 model (config 1)
+    # the toy fp32 model (4 sequences, head_dim 16)
     "tiny": lambda: make_workload(1),
 }
 

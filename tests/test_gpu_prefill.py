@@ -179,8 +179,9 @@ def test_prefill_one_row_equals_decode_row_path():
 
 
 def test_prefill_one_row_fp32_matrix_cores():
-    """Config 2's shapes (fp32, head_dim 64: fp32 matrix cores): a one-row
-    chunk agrees with the oracle's decode and with pkv_decode."""
+    """The SmolLM2-shape workload's shapes (fp32, head_dim 64: fp32 matrix
+    cores): a one-row chunk agrees with the oracle's decode and with
+    pkv_decode."""
     wl = make_workload(2, num_seqs=12)
     pc = PoolCase(wl)
     cu = np.arange(wl.num_seqs + 1, dtype=np.int32)
@@ -191,8 +192,8 @@ def test_prefill_one_row_fp32_matrix_cores():
 
 
 def test_prefill_one_row_matches_decode_matrix_cores():
-    """The same on config 5's shapes (bf16, matrix-core path): both agree with
-    the oracle's decode."""
+    """The same on the LLaMA-2-70B layer's shapes (bf16, matrix-core path):
+    both agree with the oracle's decode."""
     wl = make_workload(5, num_seqs=3)
     pc = PoolCase(wl)
     cu = np.arange(4, dtype=np.int32)
@@ -202,9 +203,10 @@ def test_prefill_one_row_matches_decode_matrix_cores():
     check_close(out_f64(pc.decode(), "bf16"), ref, "bf16", "decode")
 
 
-def test_prefill_config5_variant_sampled():
-    """Config 5's chunked-prefill variant at full size (64 sequences x 512 rows
-    at each sequence's last 512 positions); the oracle checks sampled rows."""
+def test_prefill_llama70b_layer_chunks_sampled():
+    """The LLaMA-2-70B layer workload's chunked prefill at full size (64
+    sequences x 512 rows at each sequence's last 512 positions); the oracle
+    checks sampled rows."""
     wl = make_workload(5)
     pc = PoolCase(wl)
     q_pre, cu = wl.prefill_queries()

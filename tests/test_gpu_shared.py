@@ -68,9 +68,10 @@ def _check(wl, extra=0, partition=0, exact_tail=True, fill="nan"):
     return pc, got
 
 
-def test_config2_shared_32_token_prompt():
-    """Every config 2 table starts with the same two blocks (the 32-token
-    prompt written once); a sequence shorter than 32 reads only its part."""
+def test_smollm2_shape_shared_32_token_prompt():
+    """Every table of the 30-sequence SmolLM2-shape workload starts with the
+    same two blocks (the 32-token prompt written once); a sequence shorter
+    than 32 reads only its part."""
     wl = make_workload(2)
     assert wl.groups == [(0, 30, 32)]
     _check(wl)

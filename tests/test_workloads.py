@@ -46,7 +46,7 @@ def test_structure(cfg, S):
     assert wl.q.shape == (wl.num_seqs, spec.num_q_heads, spec.head_dim)
 
 
-def test_config3_reads_exactly_32_mib():
+def test_llama1b_8x2048_reads_exactly_32_mib():
     wl = make_workload(3)
     assert wl.kv_bytes_per_call() == 33554432
 
