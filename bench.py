@@ -232,6 +232,7 @@ def time_decode_rotating(cfg: int, calls_per_set: int = 10):
     """Decode-only timing (partials + merge) cycling over disjoint block sets of
     one pool, so consecutive calls do not hit the Infinity Cache."""
     wl = make_workload(cfg)
+    print(f"[bench] rotating decode timing, {wl.name}", file=sys.stderr, flush=True)
     need = int(sum(-(-int(c) // wl.block_size) for c in wl.context_lens))
     sets = max(1, min(24, (wl.num_blocks - 1) // need))
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
@@ -615,7 +616,7 @@ def main():
     if args.layer_graph:
         pkv.load()
         for cfg in args.layer_graph:
-            print(f"[bench] 16-layer step, config {cfg}", file=sys.stderr, flush=True)
+            print(f"[bench] 16-layer step, {CONFIGS[cfg].name}", file=sys.stderr, flush=True)
             print(json.dumps({"layer_step_graph": time_layer_graph(cfg)}), flush=True)
             torch.cuda.empty_cache()
         return
@@ -637,7 +638,7 @@ def main():
               "notes)", file=sys.stderr)
         sys.exit(2)
     pkv.load()
-    print(f"[bench] generating config {args.config}", file=sys.stderr, flush=True)
+    print(f"[bench] generating {CONFIGS[args.config].name}", file=sys.stderr, flush=True)
     wl = make_workload(args.config)
     if wl.prefix_tokens:
         raise SystemExit("the timed step needs a workload without a shared prefix")
@@ -707,7 +708,6 @@ def main():
         for cfg in (3, 4):
             if cfg == args.config:
                 continue
-            print(f"[bench] rotating decode timing, config {cfg}", file=sys.stderr, flush=True)
             r = time_decode_rotating(cfg)
             extra[r.pop("name")] = r
         res["other_workloads_decode_only"] = extra
