@@ -131,17 +131,18 @@ pkv_status pkv_write(const void* k, const void* v, const int32_t* slot_mapping,
  * a bf16 result is rounded to nearest even.
  *
  * Sequences are cut into pieces of `partition` tokens (a multiple of the
- * block size; 0 picks one from the sizes, see pkv_decode_partition). With at
- * most 1024 sequences, a power-of-two partition and pieces of at least
- * 128 KiB of K and V (smaller ones finish before a schedule pays) the cut is
- * finer: each
- * context gets full pieces of `partition` tokens; a rest shorter than a
- * quarter of it joins the last full piece, a longer one becomes one or two
- * near-equal tail pieces of at most about half a partition; the launch runs
- * all full pieces first, then the tail pieces, longer ones first
- * (near-equal pieces keep every workgroup stream of the GPU equally loaded
- * and the last pieces short). Each piece of a sequence with more than one yields a partial
- * (running max m in log2 units, exp-sum l, unnormalised o) in `workspace`;
+ * block size and of the decode tile, which is 2 to 64 tokens by row size: 8
+ * at bf16 head_dim 128, 32 at bf16 head_dim 64; 0 picks one from the sizes,
+ * see pkv_decode_partition). With at most 1024 sequences, a power-of-two
+ * partition and pieces of at least 128 KiB of K and V (smaller ones finish
+ * before a schedule pays) the cut is finer: each context gets full pieces of
+ * `partition` tokens; a rest shorter than a quarter of it joins the last
+ * full piece, a longer one becomes one or two near-equal tail pieces of at
+ * most about half a partition; the launch runs all full pieces first, then
+ * the tail pieces, longer ones first (near-equal pieces keep every workgroup
+ * stream of the GPU equally loaded and the last pieces short). Each piece of
+ * a sequence with more than one yields a partial (running max m in log2
+ * units, exp-sum l, unnormalised o) in `workspace`;
  * the last workgroup of a (sequence, KV head) to finish merges them in the
  * same launch, counted by one int32 per (sequence, KV head) in a fixed
  * 256 KiB area at the start of the workspace (with more than 65536 such

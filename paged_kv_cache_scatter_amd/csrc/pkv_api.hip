@@ -161,7 +161,9 @@ pkv_status plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks
     plan->view.num_kv_heads /= 2;
     plan->view.head_dim *= 2;
   }
-  const int align = align_tokens(&plan->view);
+  // the stricter of the two alignments, so that whether a partition is valid
+  // does not depend on whether this launch pairs its heads
+  const int align = std::max(align_tokens(&plan->view), align_tokens(pool));
   int part = partition;
   if (part == 0) {
     // from the real heads: a multiple of their (coarser) alignment

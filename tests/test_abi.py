@@ -215,3 +215,13 @@ def test_piece_schedule_needs_large_pieces(lib):
     assert slots(128) == -(-4000 // 128)           # 64 KiB pieces: plain grid
     assert slots(256) == 4000 // 256 + 2           # 128 KiB pieces: schedule, up to two tails
     assert slots(1024) == 4000 // 1024 + 2         # up to two tails of 512
+
+
+def test_partition_validity_does_not_depend_on_pairing(lib):
+    """bf16 rows of 64 dims take 32-token tiles, so a partition must be a
+    multiple of 32 whether or not the launch reads its KV heads in pairs
+    (paired rows would allow 16)."""
+    d = _desc(nb=4096, bs=16, hkv=2, hd=64, dtype=1)
+    for S in (100, 512):                       # 200 pairs: unpaired; 1024: paired
+        assert lib.pkv_decode_workspace_bytes(S, 8, 100, 16, ctypes.byref(d)) == 0, S
+        assert lib.pkv_decode_workspace_bytes(S, 8, 100, 32, ctypes.byref(d)) > 0, S

@@ -40,11 +40,11 @@ def _workload(rep, seed, S=S_PAIRED, hi=600):
 @pytest.mark.parametrize("rep", [1, 2, 3, 4])
 def test_paired_decode_matches_oracle(rep):
     """One piece per sequence (automatic partition, longest first), pieces of
-    256 tokens on the piece schedule, pieces of 48 and 32 on the plain grid,
+    256 tokens on the piece schedule, pieces of 96 and 32 on the plain grid,
     and the two phases called apart (bit-equal to the one-launch call)."""
     pc = PoolCase(_workload(rep, seed=60 + rep))
     ref = pc.ref_decode()
-    for part in (0, 256, 48, 32):
+    for part in (0, 256, 96, 32):
         got = out_f64(pc.decode(partition=part), "bf16")
         check_close(got, ref, "bf16", f"rep {rep}, partition {part}")
     both = to_host(pc.decode(partition=256))
