@@ -6,16 +6,16 @@ never calls the HIP library.
 """
 
 from .pkv_oracle import (  # noqa: F401
-    attend,
+    attention,
     bf16_bits_from_f64,
     combine_partials,
     decode,
     decode_one,
-    gather_kv,
     prefill,
     prefill_one,
     slot_mapping,
     split_partials,
     storage_to_f64,
+    token_rows,
     write,
 )

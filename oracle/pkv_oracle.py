@@ -14,16 +14,19 @@ What it computes, and where the pages define it:
 * Write = scatter -- "Day 16", "What I learned" item 3 (``pool[slots] = k``);
   "Build a Mini vLLM", section 4 (prefill/decode write each token's K/V into
   ``pool.k[layer, blk, off]``).
-* Read = gather through the table, then plain attention -- "Build a Mini
-  vLLM", section 3 "PagedAttention" (``gather_kv``: the table's blocks,
-  reshaped to ``(-1, n_kv, hd)``, sliced to the sequence length;
-  ``paged_attention``: ``repeat_interleave`` of the KV heads onto the query
-  heads, scores ``q.k / sqrt(hd)``, softmax, weighted sum of V). Short tables
-  are padded with the dummy block 0, which is never read ("nano-vLLM", "How it
-  works").
-* Causal prefill -- "Build a Mini vLLM", section 4 (``full((T,T), -inf)
-  .triu(1)`` added to the scores before the softmax), applied at an offset for
-  a query chunk that ends at the sequence's last position.
+* Read through the table, then plain attention -- "Build a Mini vLLM",
+  section 3 "PagedAttention": the sequence's K/V are its positions in
+  logical order, position p sitting at offset ``p % block`` of the block the
+  table lists at ``p // block``; every query head attends the KV head of its
+  group (grouped-query attention), scores are ``q.k / sqrt(hd)``, and the
+  output is the softmax-weighted sum of the V rows. Short tables are padded
+  with the dummy block 0, which is never read ("nano-vLLM", "How it works").
+  Here the rows are looked up position by position and each query head's
+  softmax is computed on its own; the result is the same definition.
+* Causal prefill -- "Build a Mini vLLM", section 4: a query sees only keys at
+  positions up to its own (later positions are masked out before the
+  softmax), applied at an offset for a query chunk that ends at the
+  sequence's last position.
 
 Readings where the pages are silent (each also listed in the design notes):
   - ``scale`` is an argument; the pages use ``1/sqrt(head_dim)``.
@@ -124,61 +127,74 @@ def write(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray, v_new: np.n
 
 
 # --------------------------------------------------------------------------
-# gather + attention
+# reading K/V through the table, and attention
 # --------------------------------------------------------------------------
 def _clamp_ctx(ctx: int, table_len: int, block_size: int) -> int:
     return max(0, min(int(ctx), table_len * block_size))
 
 
-def gather_kv(pool: np.ndarray, table_row, ctx: int, dtype: str):
-    """Table -> (K or V as float64 ``[L, Hkv, hd]``, keep mask ``[L]``).
+def token_rows(pool: np.ndarray, table_row, ctx: int, dtype: str):
+    """The K (or V) rows of one sequence, looked up position by position.
 
-    The first ``ceil(ctx / bs)`` table entries name the sequence's blocks in
-    logical order; the rows are their concatenation cut to ``ctx``. Tokens in a
-    block whose id is not a pool block are returned as zeros with keep=False.
+    Returns ``(rows, valid)``: ``rows[p]`` (float64 ``[Hkv, hd]``) is row
+    ``p % bs`` of block ``table_row[p // bs]`` for every logical position
+    ``p < L`` (``L`` = ``ctx`` clamped to the table's reach), and ``valid[p]``
+    says whether that table entry names a pool block. Positions in a block
+    that is not in the pool have ``valid = False`` and zero rows; they take no
+    part in any softmax. Table entries past the last needed one are not read.
     """
     NB, bs, Hkv, hd = pool.shape
-    table_row = np.asarray(table_row)
+    table_row = np.asarray(table_row, dtype=np.int64)
     L = _clamp_ctx(ctx, len(table_row), bs)
-    n = -(-L // bs)
-    blocks = table_row[:n].astype(np.int64)
-    ok = (blocks >= 0) & (blocks < NB)
-    safe = np.where(ok, blocks, 0)
-    x = storage_to_f64(pool[safe], dtype).reshape(-1, Hkv, hd)[:L]
-    keep = np.repeat(ok, bs)[:L]
-    x[~keep] = 0.0
-    return x, keep
+    p = np.arange(L)
+    blk = table_row[p // bs]
+    valid = (blk >= 0) & (blk < NB)
+    rows = np.zeros((L, Hkv, hd), dtype=np.float64)
+    rows[valid] = storage_to_f64(pool[blk[valid], p[valid] % bs], dtype)
+    return rows, valid
 
 
-def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, keep=None) -> np.ndarray:
-    """One query token per head against contiguous K/V (all float64).
+def _softmax_weighted_sum(z: np.ndarray, vals: np.ndarray) -> np.ndarray:
+    """``sum_p w_p vals[p]`` with ``w = exp(z - max z) / sum exp(z - max z)``
+    along the last axis of ``z``; entries of ``z`` equal to ``-inf`` get weight 0."""
+    m = z.max(axis=-1, keepdims=True)
+    e = np.exp(z - m)
+    return (e @ vals) / e.sum(axis=-1, keepdims=True)
 
-    q ``[Hq, hd]``; K, V ``[L, Hkv, hd]``. KV heads are repeated onto the query
-    heads (query head h reads KV head h // rep), scores are ``scale * q.k``,
-    the softmax subtracts the row max, and the output is the weighted sum of V.
+
+def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
+              valid=None) -> np.ndarray:
+    """Decode attention of one token, all float64.
+
+    ``q [Hq, hd]``; ``K, V [L, Hkv, hd]``; ``valid [L]`` (default: all).
+    The query heads form ``Hkv`` groups of ``rep = Hq / Hkv`` consecutive heads;
+    head ``h`` attends KV head ``h // rep``. For each head the scores of the
+    valid positions are ``scale * (q[h] . K[p, g])``, their softmax weights the
+    rows ``V[p, g]``, and the output is that weighted sum. No valid position:
+    the output is zero.
     """
-    Hq = q.shape[0]
+    Hq, hd = q.shape
     L, Hkv, _ = K.shape
-    if keep is None:
-        keep = np.ones(L, dtype=bool)
-    if L == 0 or not keep.any():
-        return np.zeros_like(q, dtype=np.float64)
+    out = np.zeros((Hq, hd), dtype=np.float64)
+    keep = np.arange(L) if valid is None else np.nonzero(valid)[0]
+    if keep.size == 0:
+        return out
     rep = Hq // Hkv
-    Kr = np.repeat(K[keep], rep, axis=1)
-    Vr = np.repeat(V[keep], rep, axis=1)
-    scores = np.einsum("hd,lhd->hl", q, Kr) * scale
-    z = scores - scores.max(axis=-1, keepdims=True)
-    e = np.exp(z)
-    w = e / e.sum(axis=-1, keepdims=True)
-    return np.einsum("hl,lhd->hd", w, Vr)
+    for g in range(Hkv):
+        Kg = K[keep, g, :]
+        Vg = V[keep, g, :]
+        for h in range(g * rep, (g + 1) * rep):
+            out[h] = _softmax_weighted_sum(scale * (Kg @ q[h]), Vg)
+    return out
 
 
 def decode_one(q_s: np.ndarray, k_pool, v_pool, table_row, ctx: int, scale: float,
                dtype: str) -> np.ndarray:
-    """Decode output ``[Hq, hd]`` (float64) of one sequence: gather, then attend."""
-    K, keep = gather_kv(k_pool, table_row, ctx, dtype)
-    V, _ = gather_kv(v_pool, table_row, ctx, dtype)
-    return attend(storage_to_f64(q_s, dtype), K, V, scale, keep)
+    """Decode output ``[Hq, hd]`` (float64) of one sequence: its rows through
+    the table, then attention over them."""
+    K, valid = token_rows(k_pool, table_row, ctx, dtype)
+    V, _ = token_rows(v_pool, table_row, ctx, dtype)
+    return attention(storage_to_f64(q_s, dtype), K, V, scale, valid)
 
 
 def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, dtype: str,
@@ -197,25 +213,32 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, dtype: s
 # --------------------------------------------------------------------------
 def split_partials(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
                    partition: int):
-    """Per-split (m, l, o) for one sequence, float64.
+    """Per-split ``(m, l, o)`` for one sequence, float64.
 
-    Split j covers tokens ``[j*partition, (j+1)*partition)``. For every query
-    head: ``m_j`` = max score in the split, ``l_j = sum exp(score - m_j)``,
-    ``o_j = sum exp(score - m_j) * v`` (unnormalised).
+    Split j covers positions ``[j*partition, (j+1)*partition)``. For every
+    query head h (KV head ``g = h // rep``), with ``z_p = scale * q[h].K[p, g]``
+    over the split: ``m`` = the largest ``z_p``, ``l = sum_p exp(z_p - m)``,
+    ``o = sum_p exp(z_p - m) V[p, g]`` (not normalised).
+    Returns arrays ``[J, Hq]``, ``[J, Hq]``, ``[J, Hq, hd]``.
     """
-    Hq = q.shape[0]
+    Hq, hd = q.shape
     L, Hkv, _ = K.shape
     rep = Hq // Hkv
     ms, ls, os_ = [], [], []
     for j0 in range(0, L, partition):
-        Kr = np.repeat(K[j0:j0 + partition], rep, axis=1)
-        Vr = np.repeat(V[j0:j0 + partition], rep, axis=1)
-        sc = np.einsum("hd,lhd->hl", q, Kr) * scale
-        m = sc.max(axis=-1)
-        e = np.exp(sc - m[:, None])
+        m = np.zeros(Hq)
+        lsum = np.zeros(Hq)
+        o = np.zeros((Hq, hd))
+        for h in range(Hq):
+            g = h // rep
+            z = scale * (K[j0:j0 + partition, g, :] @ q[h])
+            m[h] = z.max()
+            e = np.exp(z - m[h])
+            lsum[h] = e.sum()
+            o[h] = e @ V[j0:j0 + partition, g, :]
         ms.append(m)
-        ls.append(e.sum(axis=-1))
-        os_.append(np.einsum("hl,lhd->hd", e, Vr))
+        ls.append(lsum)
+        os_.append(o)
     return np.array(ms), np.array(ls), np.array(os_)
 
 
@@ -235,33 +258,29 @@ def prefill_one(q_rows: np.ndarray, k_pool, v_pool, table_row, ctx: int, scale: 
                 dtype: str) -> np.ndarray:
     """Causal attention for the last ``n = len(q_rows)`` positions of a sequence.
 
-    Row i sits at absolute position ``a = ctx - n + i`` and attends keys
-    ``0..a``: the causal mask (``-inf`` above the diagonal) shifted by
-    ``ctx - n``. Rows with ``a < 0`` attend nothing and are zero.
+    Row i is the query at absolute position ``a_i = ctx - n + i``. It sees
+    key position p when ``p <= a_i`` (never a later position) and p lies in a
+    valid block. Each row is then decode attention over the keys it sees.
+    Rows that see no key (``a_i < 0``) are zero.
     """
-    K, keep = gather_kv(k_pool, table_row, ctx, dtype)
-    V, _ = gather_kv(v_pool, table_row, ctx, dtype)
-    L = K.shape[0]
+    K, valid = token_rows(k_pool, table_row, ctx, dtype)
+    V, _ = token_rows(v_pool, table_row, ctx, dtype)
     qf = storage_to_f64(q_rows, dtype)
     n, Hq, hd = qf.shape
     out = np.zeros((n, Hq, hd), dtype=np.float64)
-    if L == 0:
+    L, Hkv = K.shape[0], K.shape[1]
+    pos = int(ctx) - n + np.arange(n)
+    sees = (np.arange(L)[None, :] <= pos[:, None]) & valid[None, :]     # [n, L]
+    rows = np.nonzero(sees.any(axis=1))[0]
+    if rows.size == 0:
         return out
-    Hkv = K.shape[1]
     rep = Hq // Hkv
-    Kr = np.repeat(K, rep, axis=1)
-    Vr = np.repeat(V, rep, axis=1)
-    scores = np.einsum("qhd,khd->hqk", qf, Kr) * scale          # [Hq, n, L]
-    a = (int(ctx) - n) + np.arange(n)
-    allowed = (np.arange(L)[None, :] <= a[:, None]) & keep[None, :]   # [n, L]
-    mask = np.where(allowed, 0.0, -np.inf)
-    scores = scores + mask[None, :, :]
-    has = allowed.any(axis=1)                                     # rows with a key
-    mx = np.where(has[None, :, None], scores.max(axis=-1, keepdims=True), 0.0)
-    e = np.where(allowed[None], np.exp(scores - mx), 0.0)
-    den = e.sum(axis=-1, keepdims=True)
-    w = np.divide(e, den, out=np.zeros_like(e), where=den > 0)
-    out[:] = np.einsum("hqk,khd->qhd", w, Vr)
+    hidden = ~sees[rows]
+    for h in range(Hq):
+        g = h // rep
+        z = scale * (qf[rows, h, :] @ K[:, g, :].T)                     # [rows, L]
+        z[hidden] = -np.inf
+        out[rows, h, :] = _softmax_weighted_sum(z, V[:, g, :])
     return out
 
 

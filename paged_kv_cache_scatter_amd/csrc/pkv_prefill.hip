@@ -1,7 +1,7 @@
 // Attention of many query rows over the same paged keys, on matrix cores:
-//  * causal prefill ("Build a Mini vLLM" section 4: scores +
-//    full((T,T), -inf).triu(1), softmax, weighted V) for a chunk of rows that
-//    ends at each sequence's last position;
+//  * causal prefill ("Build a Mini vLLM" section 4: a query sees keys at its
+//    own and earlier positions only; softmax of the scores, weighted V) for a
+//    chunk of rows that ends at each sequence's last position;
 //  * the shared pass of the shared-prefix decode ("nano-vLLM" "Where the time
 //    went" and "Next steps": a prompt shared by many sequences is read once per
 //    step instead of once per sequence): the rows are (member, head) pairs of a

@@ -127,18 +127,20 @@ class Scheduler:
         """Step until every request is done; ``on_step(step_dict)`` runs each step's work."""
         while self.pending():
             s = self.step()
-            if on_step is not None and len(s["decode_rid"]):
+            if on_step is not None and (len(s["decode_rid"]) or len(s["prefill_rid"])):
                 on_step(s)
         return self.stats()
 
 
 def run_engine(requests, rows, num_blocks: int, block_size: int = 16, max_batch: int = 8,
                continuous: bool = True, max_blocks_per_seq: int = 64, check=None,
-               device="cuda:0"):
+               check_prefill=None, device="cuda:0"):
     """Serve ``requests`` [(rid, prompt_len, max_new, stop_after)] through the
     scheduler and the GPU kernels. ``rows`` (workloads.TokenRows) gives the K/V/q
     of every (request, position). ``check(step, out)`` may inspect each step's
-    decode output. Returns the scheduler's stats."""
+    decode output; ``check_prefill(step, out, rid_rows, pos_rows)`` each step's
+    prefill output (row i is request rid_rows[i] at position pos_rows[i]).
+    Returns the scheduler's stats."""
     dev = torch.device(device)
     dt = torch.bfloat16 if rows.dtype == "bf16" else torch.float32
     Hkv, hd = rows.k.shape[2], rows.k.shape[3]
@@ -167,10 +169,14 @@ def run_engine(requests, rows, num_blocks: int, block_size: int = 16, max_batch:
                                     tdev(cu), int(cu[-1]), block_size, num_blocks)
             _b.write(tdev(rows.k[rid_rows, pos_rows]), tdev(rows.v[rid_rows, pos_rows]), slots,
                      k_pool, v_pool)
-            _b.prefill(tdev(rows.q[rid_rows, pos_rows]), tdev(cu), k_pool, v_pool,
-                       tdev(s["prefill_tables"]), tdev(lens.astype(np.int32)), scale,
-                       int(lens.max()), int(lens.max()))
+            out_p = _b.prefill(tdev(rows.q[rid_rows, pos_rows]), tdev(cu), k_pool, v_pool,
+                               tdev(s["prefill_tables"]), tdev(lens.astype(np.int32)), scale,
+                               int(lens.max()), int(lens.max()))
+            if check_prefill is not None:
+                check_prefill(s, out_p, rid_rows, pos_rows)
         rid, pos = s["decode_rid"], s["decode_pos"]
+        if not len(rid):
+            return
         ctx = (pos + 1).astype(np.int32)
         out = _b.decode_step(tdev(rows.q[rid, pos]), tdev(rows.k[rid, pos]),
                              tdev(rows.v[rid, pos]), k_pool, v_pool, tdev(s["decode_tables"]),

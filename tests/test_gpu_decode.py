@@ -34,19 +34,16 @@ def test_decode_config_all_outputs(cfg, S):
     note(f"{pc.wl.name}: max error {err:.3e}")
 
 
-@pytest.mark.parametrize("cfg,nsample", [(4, 24), (5, 12)])
-def test_decode_full_size_sampled(cfg, nsample):
-    """Full-size configuration, default launch (as timed by the benchmark);
-    the oracle checks a sample of sequences one by one."""
+@pytest.mark.parametrize("cfg", [3, 4, 5])
+def test_decode_full_size_every_sequence(cfg):
+    """Full-size configuration in the default launch (automatic partition, the
+    piece schedule or paired heads the planner picks, as the benchmark times
+    it): every output element of every sequence against the oracle."""
     pc = _case(cfg)
     got = out_f64(pc.decode(), pc.wl.dtype)
-    rng = np.random.default_rng(cfg)
-    seqs = sorted(rng.choice(pc.wl.num_seqs, size=nsample, replace=False).tolist())
-    lens = pc.wl.context_lens
-    seqs = sorted(set(seqs) | {int(np.argmax(lens)), int(np.argmin(lens))})
-    ref = pc.ref_decode(seqs=seqs)
-    err = check_close(got[seqs], ref[seqs], pc.wl.dtype, pc.wl.name)
-    note(f"{pc.wl.name}: sampled {len(seqs)} sequences, max error {err:.3e}")
+    ref = pc.ref_decode()
+    err = check_close(got, ref, pc.wl.dtype, pc.wl.name)
+    note(f"{pc.wl.name}: all {pc.wl.num_seqs} sequences, max error {err:.3e}")
 
 
 @pytest.mark.parametrize("cfg,S,parts", [(2, None, [64, 128, 256]),

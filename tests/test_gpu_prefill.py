@@ -203,23 +203,38 @@ def test_prefill_one_row_matches_decode_matrix_cores():
     check_close(out_f64(pc.decode(), "bf16"), ref, "bf16", "decode")
 
 
-def test_prefill_llama70b_layer_chunks_sampled():
+def test_prefill_llama70b_layer_chunks():
     """The LLaMA-2-70B layer workload's chunked prefill at full size (64
-    sequences x 512 rows at each sequence's last 512 positions); the oracle
-    checks sampled rows."""
+    sequences x 512 rows at each sequence's last 512 positions), in the launch
+    the benchmark times. The oracle checks the whole chunks of the three
+    shortest and two more sequences, and of the longest sequence the first and
+    last row of every query tile (128 (row, head) pairs = 128 / group-size
+    rows per tile), plus 40 random rows of the others."""
     wl = make_workload(5)
     pc = PoolCase(wl)
     q_pre, cu = wl.prefill_queries()
-    got = out_f64(_run(pc, q_pre, cu, wl.prefill_chunk), "bf16")
+    n = wl.prefill_chunk
+    got = out_f64(_run(pc, q_pre, cu, n), "bf16")
     kp, vp = pc.ref_pools()
+    lens = wl.context_lens
+    order = np.argsort(lens, kind="stable")
     rng = np.random.default_rng(5)
-    rows = sorted(set(rng.choice(q_pre.shape[0], 40, replace=False).tolist()) |
-                  {0, 511, q_pre.shape[0] - 1})
-    for r in rows:
+    whole = [int(x) for x in order[:3]] + [int(x) for x in rng.choice(order[3:-1], 2,
+                                                                      replace=False)]
+    for s in whole:
+        a, b = int(cu[s]), int(cu[s + 1])
+        ref = oracle.prefill_one(q_pre[a:b], kp, vp, wl.block_tables[s], int(lens[s]),
+                                 wl.scale, "bf16")
+        check_close(got[a:b], ref, "bf16", f"sequence {s} (ctx {int(lens[s])}), whole chunk")
+    longest = int(order[-1])
+    tile_rows = 128 // (wl.num_q_heads // wl.num_kv_heads)
+    rows = [int(cu[longest]) + i for t in range(0, n, tile_rows) for i in (t, t + tile_rows - 1)]
+    others = [r for r in rng.choice(q_pre.shape[0], 60, replace=False).tolist()
+              if int(np.searchsorted(cu, r, side="right") - 1) not in whole + [longest]][:40]
+    for r in rows + sorted(others):
         s = int(np.searchsorted(cu, r, side="right") - 1)
-        n = int(cu[s + 1] - cu[s])
-        a = int(wl.context_lens[s]) - n + (r - int(cu[s]))
+        a = int(lens[s]) - n + (r - int(cu[s]))      # the row's absolute position
         ref = oracle.prefill_one(q_pre[r:r + 1], kp, vp, wl.block_tables[s], a + 1,
                                  wl.scale, "bf16")
-        check_close(got[r:r + 1], ref, "bf16", f"row {r}")
-    note(f"checked {len(rows)} sampled prefill rows")
+        check_close(got[r:r + 1], ref, "bf16", f"row {r} (sequence {s}, position {a})")
+    note(f"checked {len(whole)} whole chunks and {len(rows) + len(others)} more rows")

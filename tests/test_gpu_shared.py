@@ -198,17 +198,16 @@ def test_no_groups_is_plain_decode():
     assert np.array_equal(bits(to_host(out)), bits(plain))
 
 
-def test_70b_layer_64_users_of_one_prompt_sampled():
+def test_70b_layer_64_users_of_one_prompt():
     """Full size: 64 sequences of the 70B-layer shape sharing a 4096-token
-    prompt with own tails of 1..4096 tokens; 6 sequences checked against the
-    oracle, all against pkv_decode."""
+    prompt with own tails of 1..4096 tokens; every sequence against the
+    oracle (and against pkv_decode)."""
     wl = make_shared([64], [4096], ("uniform", 1, 4096), dtype=BF16, num_q_heads=64,
                      num_kv_heads=8, head_dim=128, seed=23, name="70b-64x4096-shared")
     pc = PoolCase(wl)
     gs, pl = _groups(wl)
     got = out_f64(_shared(pc, gs, pl, max_tail=_max_tail(wl, pl, gs)), wl.dtype)
+    err = check_close(got, pc.ref_decode(), wl.dtype, "vs oracle")
     plain = out_f64(pc.decode(), wl.dtype)
     check_close(got, plain, wl.dtype, "vs pkv_decode")
-    seqs = [0, 1, 17, 31, 50, 63]
-    ref = pc.ref_decode(seqs=seqs)
-    check_close(got[seqs], ref[seqs], wl.dtype, "sampled vs oracle")
+    note(f"{wl.name}: all 64 sequences, max error {err:.3e}")

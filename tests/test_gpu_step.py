@@ -180,3 +180,37 @@ def test_step_invalid_block_for_new_token():
                             oracle.slot_mapping(stabs, sfirst, scu, wl.block_size, wl.num_blocks))
     ref = oracle.decode(wl.q, kp2, vp2, bad, wl.context_lens, wl.scale, "f32")
     check_close(out_f64(out, "f32"), ref, "f32")
+
+
+@pytest.mark.parametrize("cfg", [4, 5])
+def test_step_full_size_as_benchmarked(cfg):
+    """The benchmark's timed call at full size: pkv_decode_step on every
+    sequence of the workload with the automatic partition and a zero-filled
+    workspace, the new token of each sequence at position ctx - 1. Both pools
+    are compared bit for bit with the oracle's bulk write followed by the
+    step's write, and every output element with the oracle's decode."""
+    wl = make_workload(cfg)
+    rows = _new_rows(wl)
+    pc = PoolCase(wl, exclude_last=True)
+    part = pkv.decode_partition(wl.num_seqs, pc.max_ctx, pc.k_pool)
+    ws = torch.zeros(max(16, pkv.decode_workspace_bytes(wl.num_seqs, wl.num_q_heads,
+                                                        pc.max_ctx, pc.k_pool, part)),
+                     dtype=torch.uint8, device=pc.q.device)
+    out = torch.empty_like(pc.q)
+    note(f"{wl.name}: full-size pkv_decode_step, partition {part}")
+    pkv.decode_step(pc.q, to_dev(wl.k_rows[rows]), to_dev(wl.v_rows[rows]), pc.k_pool,
+                    pc.v_pool, pc.tables, pc.ctx, wl.scale, pc.max_ctx, out=out,
+                    partition=part, workspace=ws)
+    torch.cuda.synchronize()
+    kp, vp = pc.ref_pools()
+    tabs, first, cu, srows = wl.step_segments()
+    kp, vp = oracle.write(kp, vp, wl.k_rows[srows], wl.v_rows[srows],
+                          oracle.slot_mapping(tabs, first, cu, wl.block_size, wl.num_blocks))
+    assert np.array_equal(bits(to_host(pc.k_pool)), bits(kp)), "k_pool differs from the oracle"
+    assert np.array_equal(bits(to_host(pc.v_pool)), bits(vp)), "v_pool differs from the oracle"
+    ref = oracle.decode(wl.q, kp, vp, wl.block_tables, wl.context_lens, wl.scale, wl.dtype)
+    err = check_close(oracle.storage_to_f64(to_host(out), wl.dtype), ref, wl.dtype, wl.name)
+    # the merge counters are back to zero for the next call
+    assert not to_host(ws[:256 << 10]).any()
+    note(f"{wl.name}: pools bit-exact, all {wl.num_seqs} sequences within tolerance "
+         f"(max error {err:.3e})")

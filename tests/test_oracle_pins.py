@@ -208,7 +208,7 @@ def test_attend_equals_library_sdpa(Hq, Hkv, hd, L, scale_mult):
     K = rng.standard_normal((L, Hkv, hd))
     V = rng.standard_normal((L, Hkv, hd))
     scale = scale_mult / math.sqrt(hd)
-    got = oracle.attend(q, K, V, scale)
+    got = oracle.attention(q, K, V, scale)
     ref = _sdpa(q[None], K, V, scale)[0]
     assert np.isfinite(got).all()
     np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
@@ -220,7 +220,7 @@ def test_ctx1_closed_form():
     q = rng.standard_normal((8, 16))
     K = rng.standard_normal((1, 4, 16))
     V = rng.standard_normal((1, 4, 16))
-    out = oracle.attend(q, K, V, 0.25)
+    out = oracle.attention(q, K, V, 0.25)
     for h in range(8):
         assert np.array_equal(out[h], V[0, h // 2])
 
@@ -231,12 +231,12 @@ def test_uniform_keys_give_mean_of_values():
     K = np.repeat(rng.standard_normal((1, 2, 16)), L, axis=0)
     V = rng.standard_normal((L, 2, 16))
     q = rng.standard_normal((6, 16))
-    out = oracle.attend(q, K, V, 0.3)
+    out = oracle.attention(q, K, V, 0.3)
     for h in range(6):
         np.testing.assert_allclose(out[h], V[:, h // 3].mean(axis=0), rtol=0, atol=1e-14)
     # q = 0: every score 0, same mean whatever K is
     K2 = rng.standard_normal((L, 2, 16))
-    out2 = oracle.attend(np.zeros((6, 16)), K2, V, 0.3)
+    out2 = oracle.attention(np.zeros((6, 16)), K2, V, 0.3)
     for h in range(6):
         np.testing.assert_allclose(out2[h], V[:, h // 3].mean(axis=0), rtol=0, atol=1e-14)
 
@@ -281,7 +281,7 @@ def test_paged_equals_contiguous_bit_exact(dtype):
     out = oracle.decode(wl.q, kp, vp, wl.block_tables, wl.context_lens, wl.scale, dtype)
     for s in range(len(lens)):
         K, V = _contig(wl, s)
-        ref = oracle.attend(oracle.storage_to_f64(wl.q[s], dtype), K, V, wl.scale)
+        ref = oracle.attention(oracle.storage_to_f64(wl.q[s], dtype), K, V, wl.scale)
         assert np.array_equal(out[s], ref), s
 
 
@@ -293,7 +293,7 @@ def test_block_ids_2_0_equals_contiguous_and_relabeling_is_invisible():
     kp, vp = _fill_pool(wl)
     out = oracle.decode(wl.q, kp, vp, wl.block_tables, wl.context_lens, wl.scale, "f32")
     K, V = _contig(wl, 0)
-    assert np.array_equal(out[0], oracle.attend(wl.q[0].astype(np.float64), K, V, wl.scale))
+    assert np.array_equal(out[0], oracle.attention(wl.q[0].astype(np.float64), K, V, wl.scale))
     # same logical content under another physical placement
     wl2 = make_custom([[1, 2]], [g["ctx"]], num_q_heads=4, num_kv_heads=2, head_dim=16,
                       block_size=bs, num_blocks=3, seed=9)
@@ -316,7 +316,7 @@ def test_prefix_shared_tables(ctx_a, ctx_b):
         assert np.array_equal(out[0], out[1])
     for s in range(2):
         K, V = _contig(wl, s)
-        assert np.array_equal(out[s], oracle.attend(q[s].astype(np.float64), K, V, wl.scale))
+        assert np.array_equal(out[s], oracle.attention(q[s].astype(np.float64), K, V, wl.scale))
     # the shared blocks were written once and hold the prefix rows
     assert np.array_equal(kp[1].reshape(16, -1), wl.k_rows[:16].reshape(16, -1))
 
@@ -371,7 +371,7 @@ def test_invalid_block_id_excludes_its_tokens():
     out = oracle.decode(wl.q, kp, vp, bad, wl.context_lens, wl.scale, "f32")
     K, V = _contig(wl, 0)
     keep = np.r_[0:16, 32:40]
-    ref = oracle.attend(wl.q[0].astype(np.float64), K[keep], V[keep], wl.scale)
+    ref = oracle.attention(wl.q[0].astype(np.float64), K[keep], V[keep], wl.scale)
     assert np.array_equal(out[0], ref)
 
 
@@ -385,7 +385,7 @@ def test_split_combine_equals_unsplit(partition):
     ms, ls, os_ = oracle.split_partials(q, K, V, 0.2, partition)
     assert len(ms) == -(-333 // partition)
     got = oracle.combine_partials(ms, ls, os_)
-    ref = oracle.attend(q, K, V, 0.2)
+    ref = oracle.attention(q, K, V, 0.2)
     np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-13)
     # and against the library routine, so the identity is not only self-consistent
     np.testing.assert_allclose(got, _sdpa(q[None], K, V, 0.2)[0], rtol=1e-12, atol=1e-12)
