@@ -305,7 +305,8 @@ pkv_status pkv_decode_shared(const void* q, int32_t num_seqs, int32_t num_q_head
 
 /* ---------------------------------------------------------------------------
  * pkv_prefill -- causal attention of a chunk of query rows over the pool
- * ([MV] section 4: scores + full((T,T), -inf).triu(1), softmax, weighted V).
+ * ([MV] section 4: each query sees the keys at its own and earlier positions;
+ * softmax of the scaled scores, weighted sum of V).
  *
  * Sequence s owns packed query rows cu_q[s] .. cu_q[s+1]-1 (n_s rows). Row i
  * sits at absolute position a = context_lens[s] - n_s + i and attends the
