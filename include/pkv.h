@@ -245,6 +245,35 @@ pkv_status pkv_decode_step_partials(const void* q, const void* k_new, const void
                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * pkv_decode_step_noalloc -- pkv_decode_step without a caller workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.
+ *
+ * Same computation, kernels, partition choice and result bits as
+ * pkv_decode_step with the same arguments; the split partials and merge
+ * counters live in a fixed device array of PKV_NOALLOC_SCRATCH_BYTES bytes
+ * inside the library (one per GPU, held until the process ends) instead of a
+ * passed workspace. Nothing is allocated and nothing is freed: the first call
+ * on a device looks up that device's copy of the array and clears its counter
+ * words with one small kernel on `stream`; every call leaves them zero.
+ * A call whose plan needs more than PKV_NOALLOC_SCRATCH_BYTES of scratch
+ * (pkv_decode_workspace_bytes with the same sizes) returns PKV_ERR_WORKSPACE
+ * before anything is enqueued; use pkv_decode_step with a workspace then.
+ * All calls of one process on one GPU share that GPU's array, so two calls
+ * that may run at the same time on one GPU (on two streams, from two threads)
+ * race and give wrong results: run them in stream order. (Each process has
+ * its own array.) Arguments and other errors are those of pkv_decode_step.
+ * ------------------------------------------------------------------------- */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+pkv_status pkv_decode_step_noalloc(const void* q, const void* k_new, const void* v_new,
+                                   int32_t num_seqs, int32_t num_q_heads, void* k_pool,
+                                   void* v_pool, const pkv_pool_desc* pool,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens, int32_t max_context_len,
+                                   float scale, int32_t partition, void* out, void* stream);
+
+/* ---------------------------------------------------------------------------
  * pkv_decode_shared -- paged decode for groups of sequences whose block tables
  * begin with the same blocks (a shared prompt: [NV] "Prefix caching", where
  * later users reuse the first user's full prompt blocks; [NV] "Where the time

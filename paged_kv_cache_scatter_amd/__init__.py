@@ -8,6 +8,7 @@ from ._binding import (  # noqa: F401
     BF16,
     EXPORTS,
     F32,
+    NOALLOC_SCRATCH_BYTES,
     LIB_PATH,
     PkvError,
     PoolDesc,
@@ -17,6 +18,7 @@ from ._binding import (  # noqa: F401
     decode_shared,
     decode_shared_workspace_bytes,
     decode_step,
+    decode_step_noalloc,
     decode_partition,
     decode_workspace_bytes,
     load,

@@ -28,6 +28,7 @@ _STATUS = {0: "PKV_OK", 1: "PKV_ERR_NULL", 2: "PKV_ERR_DTYPE", 3: "PKV_ERR_SHAPE
 EXPORTS = ("pkv_slot_mapping", "pkv_write", "pkv_decode_partition",
            "pkv_decode_workspace_bytes", "pkv_decode", "pkv_decode_partials",
            "pkv_decode_reduce", "pkv_decode_step", "pkv_decode_step_partials",
+           "pkv_decode_step_noalloc",
            "pkv_decode_shared_workspace_bytes", "pkv_decode_shared", "pkv_prefill",
            "pkv_block_bytes", "pkv_plan_pool", "pkv_status_string", "pkv_last_error",
            "pkv_abi_version")
@@ -81,6 +82,9 @@ def load(path: str | None = None):
         f = getattr(lib, name)
         f.argtypes = step_args
         f.restype = ctypes.c_int
+    lib.pkv_decode_step_noalloc.argtypes = [_P, _P, _P, _I, _I, _P, _P, ctypes.POINTER(PoolDesc),
+                                            _P, _I, _P, _I, ctypes.c_float, _I, _P, _P]
+    lib.pkv_decode_step_noalloc.restype = ctypes.c_int
     lib.pkv_decode_shared_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I,
                                                       ctypes.POINTER(PoolDesc)]
     lib.pkv_decode_shared_workspace_bytes.restype = ctypes.c_size_t
@@ -341,6 +345,35 @@ def decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
         fn = lib.pkv_decode_step if phase == "both" else lib.pkv_decode_step_partials
         _need(phase in ("both", "partials"), f"unknown phase {phase!r}")
         _check(fn(_ptr(q), _ptr(k_new), _ptr(v_new), S, Hq, _ptr(k_pool), _ptr(v_pool), *common))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # PKV_NOALLOC_SCRATCH_BYTES of include/pkv.h
+
+
+def decode_step_noalloc(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                        k_pool: torch.Tensor, v_pool: torch.Tensor, block_tables: torch.Tensor,
+                        context_lens: torch.Tensor, scale: float, max_context_len: int,
+                        out: torch.Tensor, partition: int = 0) -> torch.Tensor:
+    """``decode_step`` without a workspace: the library's fixed scratch array
+    holds the split partials, so nothing is allocated (``out`` must be
+    passed). Raises PkvError (PKV_ERR_WORKSPACE) when the step needs more
+    scratch than the array holds. Calls that may overlap on one GPU race."""
+    desc = _check_pools(k_pool, v_pool)
+    _dev(q, "q", k_pool.dtype)
+    _need(q.dim() == 3 and q.shape[2] == desc.head_dim, "q must be [S, Hq, head_dim]")
+    S, Hq, _ = q.shape
+    _dev(k_new, "k_new", k_pool.dtype, (S, desc.num_kv_heads, desc.head_dim))
+    _dev(v_new, "v_new", k_pool.dtype, (S, desc.num_kv_heads, desc.head_dim))
+    _dev(block_tables, "block_tables", torch.int32)
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == S,
+          "block_tables must be [S, max_blocks_per_seq]")
+    _dev(context_lens, "context_lens", torch.int32, (S,))
+    _dev(out, "out", q.dtype, q.shape)
+    _check(load().pkv_decode_step_noalloc(
+        _ptr(q), _ptr(k_new), _ptr(v_new), S, Hq, _ptr(k_pool), _ptr(v_pool), ctypes.byref(desc),
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), int(max_context_len),
+        float(scale), int(partition), _ptr(out), _stream()))
     return out
 
 

@@ -6,7 +6,9 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "pkv_internal.h"
 
@@ -392,6 +394,56 @@ pkv_status decode_impl(Phase phase, const void* q, int32_t num_seqs, int32_t num
   return PKV_OK;
 }
 
+// Scratch of pkv_decode_step_noalloc: a fixed device array (each GPU holds
+// its own copy), laid out like a decode workspace (merge counters, then
+// partials). Host code never passes the array's name to a kernel (on the host
+// it names a stand-in, not device memory): it uses the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and kept in g_noalloc_ptr.
+constexpr size_t kNoallocScratchBytes = PKV_NOALLOC_SCRATCH_BYTES;
+static_assert(kNoallocScratchBytes > kCounterBytes, "scratch holds the counter area");
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+__global__ void __launch_bounds__(256) zero_words_kernel(uint32_t* p, uint32_t n) {
+  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n; i += gridDim.x * 256u) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_noalloc_ptr[kMaxDevices];
+std::mutex g_noalloc_mu;
+
+// Device address of the current device's scratch array. The first call on a
+// device (with that device current) looks it up and clears the counter words
+// with a kernel on `st` (a kernel rather than a memset, so that a call under
+// graph capture records no memset node); every decode leaves them zero.
+pkv_status noalloc_scratch(hipStream_t st, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    set_error("no usable current device (%s, device %d)", hipGetErrorString(e), dev);
+    return PKV_ERR_HIP;
+  }
+  void* p = g_noalloc_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_noalloc_mu);
+    p = g_noalloc_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p) {
+        set_error("hipGetSymbolAddress of the scratch array failed: %s", hipGetErrorString(e));
+        return PKV_ERR_HIP;
+      }
+      hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, st,
+                         static_cast<uint32_t*>(p), (uint32_t)(kCounterBytes / 4));
+      const pkv_status ls = launch_status("zero_words_kernel");
+      if (ls != PKV_OK) return ls;
+      g_noalloc_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return PKV_OK;
+}
+
 }  // namespace
 
 void set_error(const char* fmt, ...) {
@@ -589,6 +641,37 @@ pkv_status pkv_decode_step_partials(const void* q, const void* k_new, const void
   return decode_impl(Phase::kPartials, q, num_seqs, num_q_heads, k_pool, v_pool, pool,
                      block_tables, max_blocks_per_seq, context_lens, max_context_len, scale,
                      partition, out, workspace, workspace_bytes, stream, k_new, v_new);
+}
+
+pkv_status pkv_decode_step_noalloc(const void* q, const void* k_new, const void* v_new,
+                                   int32_t num_seqs, int32_t num_q_heads, void* k_pool,
+                                   void* v_pool, const pkv_pool_desc* pool,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens, int32_t max_context_len,
+                                   float scale, int32_t partition, void* out, void* stream) {
+  if (num_seqs > 0) {
+    const pkv_status st = check_step(k_new, v_new);
+    if (st != PKV_OK) return st;
+  }
+  // the size check comes before any device call
+  DecodePlan plan;
+  pkv_status st = plan_decode(num_seqs, num_q_heads, max_blocks_per_seq, max_context_len,
+                              partition, pool, &plan);
+  if (st != PKV_OK) return st;
+  if (plan.ws_bytes > kNoallocScratchBytes) {
+    set_error("this decode step needs %zu bytes of scratch; the library's fixed area holds "
+              "%zu (call pkv_decode_step with a workspace)", plan.ws_bytes,
+              kNoallocScratchBytes);
+    return PKV_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  if (plan.ws_bytes > 0 && num_seqs > 0) {
+    st = noalloc_scratch(reinterpret_cast<hipStream_t>(stream), &ws);
+    if (st != PKV_OK) return st;
+  }
+  return decode_impl(Phase::kBoth, q, num_seqs, num_q_heads, k_pool, v_pool, pool, block_tables,
+                     max_blocks_per_seq, context_lens, max_context_len, scale, partition, out,
+                     ws, ws ? kNoallocScratchBytes : 0, stream, k_new, v_new);
 }
 
 size_t pkv_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,

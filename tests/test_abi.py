@@ -225,3 +225,24 @@ def test_partition_validity_does_not_depend_on_pairing(lib):
     for S in (100, 512):                       # 200 pairs: unpaired; 1024: paired
         assert lib.pkv_decode_workspace_bytes(S, 8, 100, 16, ctypes.byref(d)) == 0, S
         assert lib.pkv_decode_workspace_bytes(S, 8, 100, 32, ctypes.byref(d)) > 0, S
+
+
+def test_noalloc_step_refuses_plans_beyond_its_scratch(lib):
+    """pkv_decode_step_noalloc checks the scratch its plan needs against the
+    fixed area before any device call (PKV_ERR_WORKSPACE), and reports the
+    other argument errors as pkv_decode_step does."""
+    d = _desc(nb=1 << 20, bs=16, hkv=8, hd=128)
+    cap = pkv.NOALLOC_SCRATCH_BYTES
+
+    def call(S, max_ctx, part=0, q=16, kn=16):
+        maxb = -(-max_ctx // 16)
+        return lib.pkv_decode_step_noalloc(q, kn, 16, S, 64, 16, 16, ctypes.byref(d), 16, maxb,
+                                           16, max_ctx, 0.1, part, 16, None)
+
+    # 2048 sequences of 8192 tokens in 256-token pieces: far beyond 32 MiB
+    need = lib.pkv_decode_workspace_bytes(2048, 64, 8192, 256, ctypes.byref(d))
+    assert need > cap
+    assert call(2048, 8192, part=256) == 5 and "scratch" in _err(lib)
+    assert call(4, 100, q=None) == 1
+    assert call(4, 100, kn=8) == 7
+    assert call(4, 100, part=100) == 3 and "partition" in _err(lib)
