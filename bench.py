@@ -133,29 +133,63 @@ class Step:
             ev_b.record()
 
 
-def time_steps(step: Step, steps: int, warmup: int):
-    """Mean step time over ``steps`` back-to-back steps between two HIP events
-    on the launch stream, and the mean time of the decode launch alone from a
-    pair of events around it in each of another ``steps`` steps (those events
-    also hold the launch latency, so this second figure reads a few us high)."""
-    for _ in range(warmup):
-        step.run()
+MIN_WARMUP_S = 0.25   # untimed steps run for at least this long, whatever --warmup says
+
+
+def warm_up(run, warmup: int) -> int:
+    """``warmup`` untimed calls, continued until MIN_WARMUP_S of wall time has
+    passed (a fresh process's first milliseconds of GPU work run slow: 148 us
+    per step after 10 warm-up steps against 135 us after 200). Returns the
+    number of calls made."""
+    n = 0
+    t0 = time.perf_counter()
+    while n < warmup or time.perf_counter() - t0 < MIN_WARMUP_S:
+        run()
+        n += 1
+        if n % 64 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
+def timed_loop(run, calls: int) -> float:
+    """Mean ms per call of ``calls`` back-to-back calls between two HIP events
+    on the current stream (the library launches on it)."""
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
-    for _ in range(steps):
-        step.run()
+    for _ in range(calls):
+        run()
     t1.record()
     torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / steps
+    return t0.elapsed_time(t1) / calls
+
+
+def repeat_stats(ms: list) -> dict:
+    a = np.array(ms) * 1e3
+    return {"n": len(ms), "us": [round(float(x), 2) for x in a],
+            "median_us": round(float(np.median(a)), 2),
+            "p10_us": round(float(np.percentile(a, 10)), 2),
+            "p90_us": round(float(np.percentile(a, 90)), 2)}
+
+
+def time_steps(step: Step, steps: int, warmup: int, repeats: int = 3):
+    """Mean step time over ``steps`` back-to-back steps between two HIP events
+    (the headline), then ``repeats - 1`` more such loops (run-to-run spread),
+    and the mean time of the decode launch alone from a pair of events around
+    it in each of another ``steps`` steps (those events also hold the launch
+    latency, so this figure reads a few us high)."""
+    nwarm = warm_up(step.run, warmup)
+    loops = [timed_loop(step.run, steps) for _ in range(repeats)]
+    ms_step = loops[0]
     ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     for i in range(steps):
         step.run(ev_a[i], ev_b[i])
     torch.cuda.synchronize()
     each = np.array([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)])
-    return ms_step, float(each.mean()), percentiles_us(each)
+    return ms_step, float(each.mean()), percentiles_us(each), repeat_stats(loops), nwarm
 
 
 def percentiles_us(ms: np.ndarray) -> dict:
@@ -180,6 +214,56 @@ def time_cold(fn, reps: int = 20) -> dict:
     out = percentiles_us(np.array([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]))
     del scratch
     return out
+
+
+PROBE_LIB = os.path.join(ROOT, "paged_kv_cache_scatter_amd", "libpkv_probe.so")
+
+
+def time_probes(step: Step, calls: int = 20, stream_bytes: int = 2 << 30):
+    """Read-bandwidth probes with no arithmetic (libpkv_probe.so): a contiguous
+    ``stream_bytes`` buffer read once per call with 16-byte non-temporal
+    loads, and the step's own K/V rows read through its block tables in the
+    decode's order and partition. GB/s of each (the paged probe counted in the
+    step's algorithmic K/V bytes)."""
+    import ctypes
+    if not os.path.exists(PROBE_LIB):
+        raise SystemExit(f"{PROBE_LIB} is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(PROBE_LIB)
+    P, I = ctypes.c_void_p, ctypes.c_int32
+    lib.pkv_probe_stream.argtypes = [P, ctypes.c_size_t, I, P, P]
+    lib.pkv_probe_paged.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, P, P]
+    wl = step.wl
+    buf = torch.ones(stream_bytes // 4, dtype=torch.int32, device=DEV)
+    blocks = 256 * 16
+    sink = torch.zeros(1 << 20, dtype=torch.int32, device=DEV)
+    strm = torch.cuda.current_stream().cuda_stream
+
+    def stream():
+        if lib.pkv_probe_stream(buf.data_ptr(), stream_bytes, blocks, sink.data_ptr(), strm):
+            raise SystemExit("stream probe launch failed")
+
+    row_bytes = wl.head_dim * wl.itemsize
+
+    def paged():
+        if lib.pkv_probe_paged(step.k_pool.data_ptr(), step.v_pool.data_ptr(),
+                               step.tables.data_ptr(), wl.block_tables.shape[1],
+                               step.ctx.data_ptr(), wl.num_seqs, step.max_ctx,
+                               wl.num_kv_heads, row_bytes, wl.block_size, wl.num_blocks,
+                               step.partition, sink.data_ptr(), strm):
+            raise SystemExit("paged probe launch failed")
+
+    warm_up(stream, 3)
+    ms_stream = timed_loop(stream, calls)
+    warm_up(paged, 3)
+    ms_paged = timed_loop(paged, calls)
+    del buf
+    kvb = wl.kv_bytes_per_call()
+    return {"stream_GBps": round(stream_bytes / (ms_stream * 1e-3) / 1e9, 1),
+            "stream_bytes": stream_bytes, "stream_us": round(ms_stream * 1e3, 2),
+            "paged_GBps": round(kvb / (ms_paged * 1e-3) / 1e9, 1),
+            "paged_us": round(ms_paged * 1e3, 2), "paged_partition": step.partition,
+            "what": "compute-free reads: a contiguous buffer, and the step's K/V rows "
+                    "through its block tables in the decode's partition (plain split grid)"}
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
@@ -263,11 +347,16 @@ def time_decode_rotating(cfg: int, calls_per_set: int = 10):
         pkv.decode(q, k_pool, v_pool, tb, ctx, wl.scale, max_ctx, out=out, partition=part,
                    workspace=ws)
 
-    for r in range(max(sets * 2, 200)):
-        call(tables[r % sets])
-    torch.cuda.synchronize()
+    rot = [0]
+
+    def rotating():
+        call(tables[rot[0] % sets])
+        rot[0] += 1
+
+    warm_up(rotating, max(sets * 2, 200))
     n = sets * calls_per_set
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rot[0] = 0
     t0 = time.perf_counter()
     e0.record()
     for r in range(n):
@@ -277,6 +366,7 @@ def time_decode_rotating(cfg: int, calls_per_set: int = 10):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
     eager_out = out.clone()
+    loops = [ms] + [timed_loop(rotating, n) for _ in range(2)]
     # The same n calls captured in one HIP graph: replays issue no host work
     # per call, so a call shorter than the binding's host time is timed by the
     # GPU alone. Every replay must reproduce the eager bits.
@@ -316,7 +406,7 @@ def time_decode_rotating(cfg: int, calls_per_set: int = 10):
     kvb = wl.kv_bytes_per_call()
     return {"name": wl.name, "workload": workload_label(wl), "partition": part,
             "rotating_sets": sets,
-            "us_per_call": round(ms * 1e3, 2), "kv_bytes": kvb,
+            "us_per_call": round(ms * 1e3, 2), "repeats": repeat_stats(loops), "kv_bytes": kvb,
             "kv_read_GBps": round(kvb / (ms * 1e-3) / 1e9, 1),
             "pct_hbm_peak": round(100 * kvb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
             "seq_steps_per_s": round(wl.num_seqs / (ms * 1e-3), 1),
@@ -467,47 +557,159 @@ def time_layer_graph(cfg: int, layers: int = 16, steps: int = 20):
             "kv_bytes_per_step": kvb, "graph_GBps": round(kvb / (ms_graph * 1e-3) / 1e9, 1)}
 
 
-def cpu_baseline(wl, budget_s: float = 12.0, max_passes: int = 20):
-    """The fp64 oracle on the host, over the sequences of the same workload, in
-    order and in repeated passes, until ``budget_s`` of CPU time is spent. Each
-    sequence's blocks are renumbered into a compact pool (the output does not
-    depend on physical block ids); only the oracle's decode call is timed."""
-    import oracle  # test infrastructure: only this leg of the benchmark uses it
+# ---------------------------------------------------------------- CPU legs
+# The workload the CPU workers decode (set before the pool forks; the workers
+# inherit it and never touch the GPU).
+_CPU_WL = None
 
+
+def _compact_pools(wl, s):
+    """Sequence s's K/V written through the oracle into a pool of its own blocks
+    (renumbered 1..n; the output does not depend on physical block ids)."""
+    import oracle  # test infrastructure: only the CPU-baseline leg uses it
     bs = wl.block_size
-    prepared = []
-    done_bytes, done_seqs, done_tokens, spent, passes = 0, 0, 0, 0.0, 0
-    while spent < budget_s and passes < max_passes:
+    L = int(wl.context_lens[s])
+    nb = -(-L // bs)
+    shape = (nb + 1, bs, wl.num_kv_heads, wl.head_dim)
+    kp = np.zeros(shape, wl.storage_np_dtype)
+    vp = np.zeros(shape, wl.storage_np_dtype)
+    table = np.arange(1, nb + 1, dtype=np.int32)[None]
+    slots = oracle.slot_mapping(table, [0], [0, L], bs, nb + 1)
+    rows = wl.seq_rows[s]
+    kp, vp = oracle.write(kp, vp, wl.k_rows[rows], wl.v_rows[rows], slots)
+    return kp, vp, table
+
+
+def _oracle_worker(args):
+    """One CPU worker: sequences w, w + n, ... of the workload through the fp64
+    oracle, in passes, until ``budget_s`` of wall time is spent (one BLAS
+    thread per worker). Returns (sequences, context tokens, KV bytes, seconds)."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    w, n, budget_s, start_at = args
+    wl = _CPU_WL
+    mine = list(range(w, wl.num_seqs, n))
+    with threadpool_limits(1):
+        prepared = {s: _compact_pools(wl, s) for s in mine}
+        while time.time() < start_at:   # every worker starts timing together
+            time.sleep(0.001)
+        seqs = toks = nbytes = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            for s in mine:
+                kp, vp, table = prepared[s]
+                oracle.decode(wl.q[s:s + 1], kp, vp, table, wl.context_lens[s:s + 1], wl.scale,
+                              wl.dtype)
+                L = int(wl.context_lens[s])
+                seqs += 1
+                toks += L
+                nbytes += L * 2 * wl.num_kv_heads * wl.head_dim * wl.itemsize
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+        return seqs, toks, nbytes, time.perf_counter() - t0
+
+
+def host_cores() -> int:
+    """CPU threads this process may use: its affinity set, at most 16 (a
+    one-GPU machine's share of its host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, os.cpu_count() or n, 16))
+
+
+def cpu_oracle_baseline(wl, budget_s: float = 10.0, single_s: float = 4.0):
+    """The fp64 oracle on the host, over the sequences of the same workload:
+    one worker process per core (forked before this process touches the GPU),
+    each decoding its share of the sequences in passes for ``budget_s`` of
+    wall time; throughput = all workers' KV bytes / the longest worker's time.
+    Also the same on one core for ``single_s`` (``single_thread``)."""
+    import multiprocessing as mp
+    global _CPU_WL
+    _CPU_WL = wl
+    cores = min(host_cores(), wl.num_seqs)
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores) as pool:
+        start_at = time.time() + 3.0 + 0.05 * wl.num_seqs / cores   # after the pools are built
+        res = pool.map(_oracle_worker, [(w, cores, budget_s, start_at) for w in range(cores)])
+    seqs = sum(r[0] for r in res)
+    toks = sum(r[1] for r in res)
+    nbytes = sum(r[2] for r in res)
+    wall = max(r[3] for r in res)
+    one = _oracle_worker((0, 1, single_s, 0.0))
+    out = {"value": round(nbytes / wall / 1e9, 4), "unit": "GB/s", "cores": cores,
+           "kind": "oracle",
+           "sample": f"{seqs} sequence decodes of the same workload (each worker cycling over "
+                     f"its share of the {wl.num_seqs} sequences; {toks} context tokens, {nbytes} "
+                     f"KV bytes), fp64 numpy oracle, {cores} worker processes with one BLAS "
+                     f"thread each, {wall:.1f} s wall",
+           "seq_steps_per_s": round(seqs / wall, 3),
+           "host_cpu_count": os.cpu_count(),
+           "single_thread": {"value": round(one[2] / one[3] / 1e9, 4), "unit": "GB/s",
+                             "cores": 1, "sequences": one[0],
+                             "seq_steps_per_s": round(one[0] / one[3], 3),
+                             "seconds": round(one[3], 2)}}
+    _CPU_WL = None
+    return out
+
+
+def cpu_pages_plan_baseline(wl, budget_s: float = 6.0):
+    """The pages' own decode plan on the host in torch fp32 on every core:
+    each sequence's K/V gathered from one scattered pool through its block
+    table into contiguous tensors (cut to its length), then the query heads of
+    each KV head's group attend them with a batched matmul, a softmax and a
+    second batched matmul. The pool holds the workload's values upcast to
+    fp32 (the pages run fp32). Passes over the sequences until ``budget_s``."""
+    threads = host_cores()
+    prev = torch.get_num_threads()
+    torch.set_num_threads(threads)
+    try:
+        Hkv, hd, bs = wl.num_kv_heads, wl.head_dim, wl.block_size
+        rep = wl.num_q_heads // Hkv
+        kp = torch.zeros(wl.pool_shape, dtype=torch.float32)
+        vp = torch.zeros(wl.pool_shape, dtype=torch.float32)
+        kf, vf = kp.view(-1, Hkv, hd), vp.view(-1, Hkv, hd)
+        f32 = lambda a: torch.from_numpy(a.view(np.int16).astype(np.int32) << 16).view(
+            torch.float32) if wl.dtype == "bf16" else torch.from_numpy(a)
         for s in range(wl.num_seqs):
             L = int(wl.context_lens[s])
-            if len(prepared) <= s:
-                nb = -(-L // bs)
-                pool_shape = (nb + 1, bs, wl.num_kv_heads, wl.head_dim)
-                kp = np.zeros(pool_shape, wl.storage_np_dtype)
-                vp = np.zeros(pool_shape, wl.storage_np_dtype)
-                table = np.zeros((1, nb), np.int32)
-                table[0] = np.arange(1, nb + 1)
-                slots = oracle.slot_mapping(table, [0], [0, L], bs, nb + 1)
-                rows = wl.seq_rows[s]
-                kp, vp = oracle.write(kp, vp, wl.k_rows[rows], wl.v_rows[rows], slots)
-                prepared.append((kp, vp, table))
-            kp, vp, table = prepared[s]
-            t = time.perf_counter()
-            oracle.decode(wl.q[s:s + 1], kp, vp, table, wl.context_lens[s:s + 1], wl.scale,
-                          wl.dtype)
-            spent += time.perf_counter() - t
-            done_bytes += L * 2 * wl.num_kv_heads * wl.head_dim * wl.itemsize
-            done_seqs += 1
-            done_tokens += L
-            if spent >= budget_s:
-                break
-        passes += 1
-    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{done_seqs} sequence decodes ({passes} pass(es) over the {wl.num_seqs} "
-                      f"sequences of the same workload; {done_tokens} context tokens, "
-                      f"{done_bytes} KV bytes), fp64 numpy oracle, single thread, {spent:.1f} s",
-            "seq_steps_per_s": round(done_seqs / spent, 3)}
+            pos = np.arange(L)
+            slots = torch.from_numpy(wl.block_tables[s][pos // bs].astype(np.int64) * bs + pos % bs)
+            kf[slots] = f32(wl.k_rows[wl.seq_rows[s]])
+            vf[slots] = f32(wl.v_rows[wl.seq_rows[s]])
+        q = f32(wl.q).view(wl.num_seqs, Hkv, rep, hd)
+        tables = torch.from_numpy(wl.block_tables.astype(np.int64))
+
+        def one(s):
+            L = int(wl.context_lens[s])
+            nb = -(-L // bs)
+            K = kp.index_select(0, tables[s, :nb]).view(nb * bs, Hkv, hd)[:L]
+            V = vp.index_select(0, tables[s, :nb]).view(nb * bs, Hkv, hd)[:L]
+            sc = torch.bmm(q[s], K.permute(1, 2, 0)) * wl.scale         # [Hkv, rep, L]
+            return torch.bmm(torch.softmax(sc, dim=-1), V.transpose(0, 1).contiguous())
+
+        one(0)
+        seqs = toks = nbytes = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            for s in range(wl.num_seqs):
+                one(s)
+                L = int(wl.context_lens[s])
+                seqs += 1
+                toks += L
+                nbytes += L * 2 * Hkv * hd * wl.itemsize
+        wall = time.perf_counter() - t0
+    finally:
+        torch.set_num_threads(prev)
+    return {"value": round(nbytes / wall / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "pages_plan_fp32",
+            "sample": f"{seqs} sequence decodes ({seqs // max(wl.num_seqs, 1)} passes over the "
+                      f"{wl.num_seqs} sequences; {toks} context tokens): table gather into "
+                      f"contiguous K/V, then grouped bmm-softmax-bmm, torch fp32 on "
+                      f"{threads} threads, {wall:.1f} s; bytes counted at the workload's "
+                      f"{wl.dtype} size",
+            "seq_steps_per_s": round(seqs / wall, 3)}
 
 
 def traffic_from_counters(kernel_src: str):
@@ -637,16 +839,25 @@ def main():
               "(the path shards by sequence or KV head with no exchange; see the design "
               "notes)", file=sys.stderr)
         sys.exit(2)
-    pkv.load()
     print(f"[bench] generating {CONFIGS[args.config].name}", file=sys.stderr, flush=True)
     wl = make_workload(args.config)
     if wl.prefix_tokens:
         raise SystemExit("the timed step needs a workload without a shared prefix")
+    cpu_legs = {}
+    if not args.no_cpu:
+        # before this process touches the GPU: the oracle's worker processes are forked
+        print("[bench] CPU legs: the oracle on every core, the pages' plan in torch fp32",
+              file=sys.stderr, flush=True)
+        cpu_legs["cpu_baseline"] = cpu_oracle_baseline(wl)
+        cpu_legs["cpu_pages_plan_fp32"] = cpu_pages_plan_baseline(wl)
+    pkv.load()
     step = Step(wl, args.partition)
-    print(f"[bench] timing {args.steps} steps (warmup {args.warmup}), partition "
-          f"{step.partition}", file=sys.stderr, flush=True)
-    ms_step, ms_bracketed, pct_launch = time_steps(step, args.steps, args.warmup)
+    print(f"[bench] timing {args.steps} steps (warmup {args.warmup}, at least "
+          f"{MIN_WARMUP_S} s), partition {step.partition}", file=sys.stderr, flush=True)
+    ms_step, ms_bracketed, pct_launch, reps, nwarm = time_steps(step, args.steps, args.warmup)
     cold = time_cold(step.run)
+    print("[bench] read-bandwidth probes", file=sys.stderr, flush=True)
+    probe = time_probes(step)
     kvb = wl.kv_bytes_per_call()
     gbs = kvb / (ms_step * 1e-3) / 1e9
     # the fused step is one launch of the decode kernel: its mean launch
@@ -680,11 +891,17 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "decode_partials_kernel (fused step)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "pct_of_stream_probe": round(achieved / probe["stream_GBps"], 4),
+                     "pct_of_paged_probe": round(achieved / probe["paged_GBps"], 4),
                      "kernel_ms": round(ms_kernel, 5),
                      "kernel_ms_events_around_each_launch": round(ms_bracketed, 5),
                      "algorithmic_bytes_per_launch": kvb},
         # spread of the launches timed one by one (events around each), and
         # single launches after a cache-evicting write ("cold")
+        "warmup_steps_run": nwarm,
+        # the headline loop and two more identical loops (run-to-run spread)
+        "repeats": reps,
+        "probe": probe,
         "launch_us_percentiles": pct_launch,
         "cold_launch_us_percentiles": cold,
     }
@@ -696,7 +913,7 @@ def main():
         torch.cuda.empty_cache()
         print("[bench] the same step with separate write launches", file=sys.stderr, flush=True)
         sep = Step(wl, args.partition, fused=False)
-        ms_sep, ms_sep_k, _ = time_steps(sep, args.steps, args.warmup)
+        ms_sep, ms_sep_k, _, _, _ = time_steps(sep, args.steps, args.warmup, repeats=1)
         res["separate_write_step"] = {
             "step": "pkv_slot_mapping + pkv_write + pkv_decode (split decode and merge, "
                     "one launch)",
@@ -711,10 +928,7 @@ def main():
             r = time_decode_rotating(cfg)
             extra[r.pop("name")] = r
         res["other_workloads_decode_only"] = extra
-    if not args.no_cpu:
-        print("[bench] CPU oracle sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(wl)
-        res["cpu_baseline"]["host_cpu_count"] = os.cpu_count()
+    res.update(cpu_legs)
     print(json.dumps(res), flush=True)
 
 

@@ -1,7 +1,8 @@
 """Build libpkv.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
 Every source is compiled to an object in parallel, then linked in-tree into
-``paged_kv_cache_scatter_amd/libpkv.so``. Run as ``python -m
+``paged_kv_cache_scatter_amd/libpkv.so``; the benchmark's read-bandwidth
+probes go into ``libpkv_probe.so`` beside it. Run as ``python -m
 paged_kv_cache_scatter_amd.build``.
 """
 
@@ -18,6 +19,9 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpkv.so")
 SOURCES = ["pkv_api.hip", "pkv_write.hip", "pkv_decode.hip", "pkv_prefill.hip"]
 HOST_SOURCES = ["pkv_sched.cpp"]   # host-only C++ (the scheduler above the kernels)
+# read-bandwidth probes for the benchmark, in a library of their own
+PROBE_SOURCE = "pkv_probe.hip"
+PROBE_LIB = os.path.join(PKG, "libpkv_probe.so")
 ARCH = "gfx950"
 
 # Packed-fp32 VALU ops are switched off for the device code; hipcc's host pass
@@ -64,9 +68,12 @@ def build(verbose: bool = False) -> str:
         cmds.append([cxx(), "-O2", "-std=c++17", "-fPIC", "-Wall", "-c", os.path.join(CSRC, s),
                      "-o", o])
         objs.append(o)
+    probe_tmp = PROBE_LIB + ".tmp"
+    cmds.append([cc, *FLAGS, "-shared", os.path.join(CSRC, PROBE_SOURCE), "-o", probe_tmp])
     workers = min(len(cmds), max(1, (os.cpu_count() or 4)))
     with ThreadPoolExecutor(max_workers=workers) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
+    os.replace(probe_tmp, PROBE_LIB)
     tmp = LIB + ".tmp"
     _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)

@@ -1,0 +1,143 @@
+// Read-bandwidth probes for the benchmark (libpkv_probe.so; not part of the
+// attention path). They measure what this GPU delivers for two access
+// patterns with no arithmetic, so that the decode kernel can be reported as a
+// fraction of a measured ceiling as well as of the published HBM peak:
+//  * stream: a contiguous buffer read once with 16-byte loads;
+//  * paged:  the K and V rows of every (sequence, KV head) read through the
+//            block table in the decode's order (one workgroup per (KV head,
+//            sequence, split of `partition` tokens), each wave taking 16-byte
+//            pieces of consecutive token rows), as the decode reads them.
+// Loaded values are folded into one word per thread that is stored only if it
+// equals a value the data cannot produce, so no load can be dropped and
+// almost nothing is written.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr int kThreads = 256;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load with the non-temporal hint (a stream read once)
+__device__ __forceinline__ uint4 ld_nt(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void sink_if_impossible(uint32_t acc, uint32_t* sink) {
+  // acc == 0x7FBADBAD is not reachable in practice; the compare keeps the loads
+  if (acc == 0x7FBADBADu) sink[blockIdx.x] = acc;
+}
+
+__global__ void __launch_bounds__(kThreads) stream_probe_kernel(const uint4* buf, size_t n16,
+                                                                uint32_t* sink) {
+  uint32_t acc = 0;
+  const size_t stride = (size_t)gridDim.x * kThreads;
+  size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  // four loads in flight per thread
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = ld_nt(buf + i), b = ld_nt(buf + i + stride), c = ld_nt(buf + i + 2 * stride),
+                d = ld_nt(buf + i + 3 * stride);
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^
+           d.w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = ld_nt(buf + i);
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  sink_if_impossible(acc, sink);
+}
+
+struct PagedArgs {
+  const char* k_pool;
+  const char* v_pool;
+  const int32_t* tables;
+  const int32_t* ctx_lens;
+  uint32_t* sink;
+  int32_t max_blocks, num_seqs, num_kv_heads, row_bytes, block_shift, partition, num_blocks;
+};
+
+// One workgroup per (KV head g, sequence s, split j). Lanes of a wave cover
+// LPT = row_bytes / 16 consecutive 16-byte pieces of one token's row, so a
+// wave reads 64 / LPT consecutive tokens per load; the four waves interleave
+// by load. Tokens past the context or in an invalid block are skipped.
+__global__ void __launch_bounds__(kThreads) paged_probe_kernel(PagedArgs a) {
+  const int g = blockIdx.x, s = blockIdx.y, j = blockIdx.z;
+  int ctx = a.ctx_lens[s];
+  const int reach = a.max_blocks << a.block_shift;   // positions the table covers
+  ctx = ctx < 0 ? 0 : (ctx > reach ? reach : ctx);
+  const int t0 = j * a.partition;
+  if (t0 >= ctx) return;
+  const int t1 = min(ctx, t0 + a.partition);
+  const int lpt = a.row_bytes / 16;          // lanes per token row (<= 64)
+  const int tpl = kThreads / lpt;            // tokens per workgroup load
+  const int piece = threadIdx.x % lpt;
+  const size_t rsb = (size_t)a.num_kv_heads * a.row_bytes;   // bytes of one token (all heads)
+  const size_t head_off = (size_t)g * a.row_bytes + (size_t)piece * 16;
+  const int32_t* trow = a.tables + (size_t)s * a.max_blocks;
+  const int bmask = (1 << a.block_shift) - 1;
+  uint32_t acc = 0;
+  for (int t = t0 + threadIdx.x / lpt; t < t1; t += tpl) {
+    const int blk = trow[t >> a.block_shift];
+    if ((unsigned)blk >= (unsigned)a.num_blocks) continue;
+    const size_t off = (((size_t)blk << a.block_shift) + (size_t)(t & bmask)) * rsb + head_off;
+    const uint4 k = ld_nt(reinterpret_cast<const uint4*>(a.k_pool + off));
+    const uint4 v = ld_nt(reinterpret_cast<const uint4*>(a.v_pool + off));
+    acc ^= k.x ^ k.y ^ k.z ^ k.w ^ v.x ^ v.y ^ v.z ^ v.w;
+  }
+  sink_if_impossible(acc, a.sink);
+}
+
+int status(hipError_t e) { return e == hipSuccess ? 0 : 6; }
+
+}  // namespace
+
+extern "C" {
+
+// Reads `bytes` (a multiple of 16, 16-byte aligned) of `buf` once; `sink` needs
+// `blocks` uint32 words (nothing is normally written there). 0 on success,
+// 3 on bad sizes, 6 if the launch failed.
+int pkv_probe_stream(const void* buf, size_t bytes, int32_t blocks, void* sink, void* stream) {
+  if (!buf || !sink || bytes % 16 || ((uintptr_t)buf & 15) || blocks < 1) return 3;
+  hipLaunchKernelGGL(stream_probe_kernel, dim3(blocks), dim3(kThreads), 0,
+                     reinterpret_cast<hipStream_t>(stream), static_cast<const uint4*>(buf),
+                     bytes / 16, static_cast<uint32_t*>(sink));
+  return status(hipGetLastError());
+}
+
+// Reads K and V of positions < context_lens[s] of every sequence and KV head
+// through `tables` (the decode's pool layout [num_blocks, block_size,
+// num_kv_heads, row_bytes]). row_bytes: bytes of one KV head's row (a multiple
+// of 16, at most 1024); block_size a power of two; `sink` needs
+// num_kv_heads * num_seqs * ceil(max_ctx / partition) words.
+int pkv_probe_paged(const void* k_pool, const void* v_pool, const int32_t* tables,
+                    int32_t max_blocks, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t max_ctx, int32_t num_kv_heads, int32_t row_bytes, int32_t block_size,
+                    int32_t num_blocks, int32_t partition, void* sink, void* stream) {
+  if (!k_pool || !v_pool || !tables || !context_lens || !sink || num_seqs < 1 ||
+      num_seqs > 65535 || num_kv_heads < 1 || row_bytes < 16 || row_bytes % 16 ||
+      row_bytes > 1024 || block_size < 1 || (block_size & (block_size - 1)) || partition < 1 ||
+      max_ctx < 1 || num_blocks < 1 || max_blocks < 1)
+    return 3;
+  PagedArgs a;
+  a.k_pool = static_cast<const char*>(k_pool);
+  a.v_pool = static_cast<const char*>(v_pool);
+  a.tables = tables;
+  a.ctx_lens = context_lens;
+  a.sink = static_cast<uint32_t*>(sink);
+  a.max_blocks = max_blocks;
+  a.num_seqs = num_seqs;
+  a.num_kv_heads = num_kv_heads;
+  a.row_bytes = row_bytes;
+  a.block_shift = __builtin_ctz((unsigned)block_size);
+  a.partition = partition;
+  a.num_blocks = num_blocks;
+  const int splits = (max_ctx + partition - 1) / partition;
+  if (splits > 65535) return 3;
+  hipLaunchKernelGGL(paged_probe_kernel, dim3(num_kv_heads, num_seqs, splits), dim3(kThreads), 0,
+                     reinterpret_cast<hipStream_t>(stream), a);
+  return status(hipGetLastError());
+}
+
+}  // extern "C"
