@@ -310,9 +310,14 @@ pkv_status pkv_decode_step_noalloc(const void* q, const void* k_new, const void*
  *   pkv_decode; the
  *   tail launch merges the shared and tail partials, so a call is two launches
  *   (shared pass, tails + merge).
- * With num_groups == 0, max_prefix_len < block_size, or a shape the shared
+ * With num_groups == 0, max_prefix_len < block_size, a shape the shared
  * pass does not compile (it covers bf16 and fp32 pools, head_dim 64 and 128,
- * group size 1..8), the call is exactly pkv_decode. Errors are those of
+ * group size 1..8), or when the reads the shared pass could save at most,
+ * (num_seqs - num_groups) * max_prefix_len * 2 * num_kv_heads * head_dim *
+ * itemsize bytes, are below 64 MiB (one launch of plain decode is then
+ * faster than the extra shared-pass launch; the environment variable
+ * PKV_SHARED_MIN_SAVED_BYTES, read at each call, sets another bound, 0 for
+ * always), the call is exactly pkv_decode. Errors are those of
  * pkv_decode, plus PKV_ERR_SHAPE for inconsistent group sizes and
  * PKV_ERR_NULL for a NULL group_start / prefix_lens when num_groups > 0.
  * ------------------------------------------------------------------------- */

@@ -3,6 +3,7 @@
 // synchronisation, no device reads.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -93,6 +94,7 @@ int align_tokens(const pkv_pool_desc* pool) {
 }
 
 int auto_partition(int num_seqs, int max_ctx, const pkv_pool_desc* pool) {
+  const int cus = num_cus();
   const int align = align_tokens(pool);
   const int whole = ((std::max(max_ctx, 1) + align - 1) / align) * align;   // one split covers all
   const int cap = (kMaxPartition / align) * align;
@@ -105,10 +107,10 @@ int auto_partition(int num_seqs, int max_ctx, const pkv_pool_desc* pool) {
   // splits 150 us, 512-token 172 us, 2048-token 164 us.
   const double units = (double)num_seqs * pool->num_kv_heads;
   int part;
-  if (units >= 4.0 * kNumCUs) {
+  if (units >= 4.0 * cus) {
     part = whole;
   } else {
-    const double p = units * (double)max_ctx / (16.0 * kNumCUs);
+    const double p = units * (double)max_ctx / (16.0 * cus);
     part = 256;
     while (part < p && part < cap) part <<= 1;
   }
@@ -127,7 +129,7 @@ int auto_partition(int num_seqs, int max_ctx, const pkv_pool_desc* pool) {
 // 2048 tokens (64 pairs) 16.0 us against 14.8 us.
 bool pair_heads(const pkv_pool_desc* pool, int num_seqs, int rep) {
   return pool->dtype == PKV_BF16 && pool->head_dim == 64 && pool->num_kv_heads % 2 == 0 &&
-         rep <= 4 && (double)num_seqs * pool->num_kv_heads >= 4.0 * kNumCUs;
+         rep <= 4 && (double)num_seqs * pool->num_kv_heads >= 4.0 * num_cus();
 }
 
 pkv_status plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
@@ -224,6 +226,21 @@ struct SharedIn {
   int32_t num_groups, max_group, max_prefix, max_tail;
 };
 
+// Least K/V bytes a shared pass must be able to save for pkv_decode_shared to
+// run it (environment PKV_SHARED_MIN_SAVED_BYTES overrides; 0 always runs
+// it). Measured: 30 users of a 500-token prompt at the SmolLM2-135M shape
+// save at most 22 MB per call and ran 15.6 us plain against 21.3 us shared;
+// 64 users of a 4096-token prompt at the LLaMA-2-70B layer shape save 1.06 GB
+// and ran 294 us plain against 166 us shared.
+constexpr int64_t kSharedMinSavedBytes = 64ll << 20;
+int64_t shared_min_saved_bytes() {
+  const char* e = getenv("PKV_SHARED_MIN_SAVED_BYTES");
+  if (!e || !*e) return kSharedMinSavedBytes;
+  char* end = nullptr;
+  const long long v = strtoll(e, &end, 10);
+  return (end && *end == '\0' && v >= 0) ? (int64_t)v : kSharedMinSavedBytes;
+}
+
 // Shared-prefix plan: the tail splits (partition from the longest tail), then
 // the shared pass's key splits, sized for about two workgroups per CU.
 // sd->group_start stays NULL when the shared pass is not used (no groups, a
@@ -247,6 +264,12 @@ pkv_status plan_shared(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks
   if (in.num_groups == 0 || in.max_prefix < bs ||
       !shared_pass_supported(pool->dtype, pool->head_dim, num_q_heads / pool->num_kv_heads))
     return PKV_OK;
+  // The shared pass is a launch of its own; it pays only when the reads it
+  // saves cover it. At most every member but one per group skips the prompt:
+  // (num_seqs - num_groups) * max_prefix rows of K and V.
+  const int64_t saved = (int64_t)(num_seqs - in.num_groups) * in.max_prefix * 2 *
+                        pool->num_kv_heads * pool->head_dim * dtype_bytes(pool->dtype);
+  if (saved < shared_min_saved_bytes()) return PKV_OK;
   const int tail = in.max_tail < 0 ? max_ctx : in.max_tail;
   st = plan_decode(num_seqs, num_q_heads, max_blocks, tail, partition, pool, plan, false, false);
   if (st != PKV_OK) return st;
@@ -254,7 +277,8 @@ pkv_status plan_shared(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks
   const int64_t row_tiles = ((int64_t)in.max_group * plan->rep + kSharedRows - 1) / kSharedRows;
   const int64_t base = (int64_t)in.num_groups * pool->num_kv_heads * row_tiles;
   const int64_t max_ks = (in.max_prefix + align - 1) / align;
-  const int64_t nks = std::min(std::max<int64_t>((2 * kNumCUs + base - 1) / base, 1), max_ks);
+  const int64_t cus = num_cus();
+  const int64_t nks = std::min(std::max<int64_t>((2 * cus + base - 1) / base, 1), max_ks);
   int64_t pp = ((in.max_prefix + nks - 1) / nks + align - 1) / align * align;
   pp = std::min(pp, (int64_t)kSharedMaxTbl * bs / align * align);
   const int64_t jp = (in.max_prefix + pp - 1) / pp;
@@ -451,6 +475,24 @@ void set_error(const char* fmt, ...) {
   va_start(ap, fmt);
   vsnprintf(g_err, sizeof(g_err), fmt, ap);
   va_end(ap);
+}
+
+int num_cus() {
+  static std::atomic<int> cached[64];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();   // leave no error behind for a later launch check
+    return kDefaultCUs;
+  }
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n < 1) {
+    (void)hipGetLastError();
+    n = kDefaultCUs;
+  }
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 pkv_status launch_status(const char* what) {

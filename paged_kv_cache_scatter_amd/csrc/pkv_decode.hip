@@ -696,14 +696,6 @@ struct Lds {
   }
 };
 
-// Device-coherent (agent-scope) store and load of one float: the store is
-// written through the XCD's L2, the load is not served from a stale L2 line.
-__device__ __forceinline__ void st_agent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_agent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // Merge of one (sequence, KV head)'s split partials into the output rows of
 // its REP query heads: M = max m_i, L = sum l_i 2^(m_i - M), out = sum
@@ -715,11 +707,6 @@ __device__ __forceinline__ float ld_agent(const float* p) {
 // kernel). wl is the wave's 64-float LDS scratch (more than 64 partials).
 constexpr int kMergeBatch = 8;
 
-__device__ __forceinline__ float2 ld_agent2(const float* p) {
-  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)),
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
-}
 
 template <typename T, int HD, int REP, int PR>
 __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int hq0, int nps,
@@ -1285,15 +1272,31 @@ decode_partials_kernel(DecodeArgs a) {
   // Each wave waits until its device-coherent partial stores are complete
   // before the barrier; only then is the workgroup counted, so a workgroup
   // that sees the full count reads every partial back with device-coherent
-  // loads. (No cache-wide write-back or invalidate is needed: the partials
-  // never sit dirty in an L2, and the loads do not take stale L2 lines.)
+  // loads. The atomics are relaxed, so the ordering comes from how gfx950
+  // executes them, which the merge relies on (the GFX942 memory model that
+  // LLVM's AMDGPU backend documents and applies to gfx950; a CPU test compiles
+  // these helpers and checks the first three):
+  //  1. an agent-scope atomic store is a global store with sc1 set: it is
+  //     written through the XCD's own L2 (L2s of different XCDs are not
+  //     coherent with each other), so no partial sits dirty in one L2;
+  //  2. an agent-scope atomic load is a global load with sc1 set: it is not
+  //     served from a line the reading XCD's L2 may hold stale;
+  //  3. the counter is a returning global atomic add at agent scope, which
+  //     the memory system performs at the device's coherence point;
+  //  4. on this GFX9-family target vmcnt counts stores too, and a store's
+  //     count is released only when the memory system has acknowledged it,
+  //     so s_waitcnt vmcnt(0) followed by the barrier puts every wave's
+  //     partial stores before the counting add.
+  // With these, no cache-wide write-back or invalidate is needed (an
+  // agent-scope release/acquire pair would emit buffer_wbl2 / buffer_inv of
+  // the whole L2 per workgroup: measured 660 us per launch instead of 173).
   wait_vmcnt<0>();
   int* last = reinterpret_cast<int*>(smem) + kWaves * 64;
   __syncthreads();
   if (nsplit > 1) {
     if (tid == 0) {
       int* cnt = a.counters + (size_t)s * a.num_kv_heads + g;
-      const int before = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int before = count_agent(cnt);
       *last = before == nsplit - 1;
       // every split has counted: reset for the next launch
       if (before == nsplit - 1) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -13,7 +13,13 @@ namespace pkv {
 void set_error(const char* fmt, ...);   // records the thread-local message
 pkv_status launch_status(const char* what);  // hipGetLastError -> status
 
-constexpr int kNumCUs = 256;   // MI355X compute units (8 XCDs x 32)
+// Compute units of the current device, looked up once per device with
+// hipDeviceGetAttribute (the planners size their split counts and head pairing
+// to it, so a device partitioned into fewer CUs gets its own plan). When no
+// device is visible (a planning-only call on a host without a GPU) it is
+// kDefaultCUs, MI355X's 256 (8 XCDs x 32).
+constexpr int kDefaultCUs = 256;
+int num_cus();
 
 struct SlotArgs {
   const int32_t* tables;
@@ -307,33 +313,59 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 }
 
 // Direct-to-LDS staging: global_load_lds_dwordx4 writes lane i's 16 bytes
-// at LDS address M0 + 16*i, without passing through registers. The compiler
-// does not see these writes, so the waits on them are explicit.
+// at LDS address M0 + 16*i, without passing through registers. The LDS
+// address is an M0 operand of the asm ("{m0}"), so the compiler writes M0
+// itself and knows the statement reads it; the s_nop covers the wait state
+// between that write and the load. The compiler does not see the LDS writes,
+// so the waits on them are explicit. (The compiler builtin for these loads
+// was measured slower: it tail-merges loads into 64-bit per-lane addresses and
+// changes the waits; 94.2 against 82.0 us on the 192-sequence Llama-3.2-1B
+// decode.)
 // NT: non-temporal hint, for rows read once in a stream larger than the
 // caches (the decode's K/V rows).
 template <bool NT = false>
 __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds) {
   if constexpr (NT)
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
-                 :: "v"(gaddr), "s"(lds) : "memory");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :: "v"(gaddr), "{m0}"(lds) : "memory");
   else
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(gaddr), "s"(lds) : "memory");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(gaddr), "{m0}"(lds) : "memory");
 }
 template <bool NT = false>
 __device__ __forceinline__ void dma16s(const char* sbase, uint32_t voff, uint32_t lds) {
   if constexpr (NT)
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
-                 :: "v"(voff), "s"(sbase), "s"(lds) : "memory");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :: "v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
   else
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :: "v"(voff), "s"(sbase), "s"(lds) : "memory");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
 }
 // The same for one 4-byte word per lane (lane i -> M0 + 4*i).
 __device__ __forceinline__ void dma4(const void* gaddr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :: "v"(gaddr), "s"(lds) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(gaddr), "{m0}"(lds) : "memory");
 }
+// Device-coherent (agent-scope) store and loads of fp32 partials, read back
+// in the same launch by a workgroup that may run on another XCD: the store is
+// written through the XCD's L2, the loads are not served from a stale L2
+// line (the in-launch merge of the decode kernel states what it relies on).
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 ld_agent2(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+// The merge counter's add: returns the count before this workgroup's.
+__device__ __forceinline__ int count_agent(int* p) {
+  return __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");

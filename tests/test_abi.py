@@ -140,7 +140,8 @@ def _shared_ws(lib, d, S=64, Hq=64, max_ctx=4096, G=1, mg=64, mp=2048, mt=2048, 
                                                  ctypes.byref(d))
 
 
-def test_shared_prefix_plan(lib):
+def test_shared_prefix_plan(lib, monkeypatch):
+    monkeypatch.delenv("PKV_SHARED_MIN_SAVED_BYTES", raising=False)
     d = _desc(nb=32769, bs=16, hkv=8, hd=128)
     # tails: 2 splits of 1024 tokens; shared pass: 1 group x 8 KV heads x 4 row
     # tiles (64 members x 8 heads / 128 rows) = 32 units, so 16 key splits of
@@ -161,7 +162,8 @@ def test_shared_prefix_plan(lib):
         assert _shared_ws(lib, d, **kw) == 0, kw
 
 
-def test_shared_prefix_argument_errors(lib):
+def test_shared_prefix_argument_errors(lib, monkeypatch):
+    monkeypatch.setenv("PKV_SHARED_MIN_SAVED_BYTES", "0")   # small sizes: still share
     d = _desc(nb=64, bs=16, hkv=8, hd=128)
 
     def call(gs=16, pl=16, G=1, mg=4, mp=64, mt=-1, S=4, ws=16, wsb=1 << 30):
@@ -246,3 +248,22 @@ def test_noalloc_step_refuses_plans_beyond_its_scratch(lib):
     assert call(4, 100, q=None) == 1
     assert call(4, 100, kn=8) == 7
     assert call(4, 100, part=100) == 3 and "partition" in _err(lib)
+
+
+def test_shared_prefix_planner_falls_back_below_the_saved_bytes_bound(lib, monkeypatch):
+    """pkv_decode_shared plans plain decode (the same workspace as
+    pkv_decode) when the reads a shared pass could save, (S - G) * prefix *
+    2 * Hkv * hd * itemsize, are under 64 MiB or PKV_SHARED_MIN_SAVED_BYTES."""
+    monkeypatch.delenv("PKV_SHARED_MIN_SAVED_BYTES", raising=False)
+    d = _desc(nb=4096, bs=16, hkv=3, hd=64, dtype=0)      # SmolLM2-135M shape, fp32
+    plain = lib.pkv_decode_workspace_bytes(30, 9, 704, 0, ctypes.byref(d))
+    shared = lambda: lib.pkv_decode_shared_workspace_bytes(30, 9, 704, 1, 30, 496, 208, 0,
+                                                           ctypes.byref(d))
+    # 29 * 496 * 2 * 3 * 64 * 4 = 22,093,824 bytes: plain decode
+    assert shared() == plain
+    monkeypatch.setenv("PKV_SHARED_MIN_SAVED_BYTES", "0")
+    assert shared() > plain
+    monkeypatch.setenv("PKV_SHARED_MIN_SAVED_BYTES", str(22093824))     # exactly the bound
+    assert shared() > plain
+    monkeypatch.setenv("PKV_SHARED_MIN_SAVED_BYTES", str(22093825))
+    assert shared() == plain

@@ -17,6 +17,14 @@ from _gpu_util import PoolCase, bits, check_close, note, out_f64, to_dev, to_hos
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(autouse=True)
+def _always_share(monkeypatch):
+    """These cases are far smaller than the 64 MiB of saved reads at which the
+    planner starts using the shared pass; run the shared pass on them anyway
+    (the planner's choice itself is checked in test_default_rule_*)."""
+    monkeypatch.setenv("PKV_SHARED_MIN_SAVED_BYTES", "0")
+
+
 def _groups(wl, extra=0):
     """group_start [G+1] and prefix_lens [G] of the workload's groups (every
     sequence in one group; ``extra`` is added to each prefix length)."""
@@ -211,3 +219,21 @@ def test_70b_layer_64_users_of_one_prompt():
     plain = out_f64(pc.decode(), wl.dtype)
     check_close(got, plain, wl.dtype, "vs pkv_decode")
     note(f"{wl.name}: all 64 sequences, max error {err:.3e}")
+
+
+def test_default_rule_runs_plain_decode_at_the_pages_scale(monkeypatch):
+    """With the default bound, 30 users of a 496-token shared prompt at the
+    SmolLM2-135M shape (at most 22 MB of reads saved) run plain decode: the
+    same bits as pkv_decode; with the bound at 0 they take the shared pass and
+    stay within tolerance of the oracle."""
+    monkeypatch.delenv("PKV_SHARED_MIN_SAVED_BYTES")
+    wl = make_shared([30], [496], ("uniform", 12, 204), dtype=F32, num_q_heads=9,
+                     num_kv_heads=3, head_dim=64, seed=21, name="smollm2-500-shared")
+    pc = PoolCase(wl)
+    gs, pl = _groups(wl)
+    plain = to_host(pc.decode())
+    got = to_host(_shared(pc, gs, pl, max_tail=_max_tail(wl, pl, gs)))
+    assert np.array_equal(bits(got), bits(plain))
+    monkeypatch.setenv("PKV_SHARED_MIN_SAVED_BYTES", "0")
+    shared = out_f64(_shared(pc, gs, pl, max_tail=_max_tail(wl, pl, gs)), wl.dtype)
+    check_close(shared, pc.ref_decode(), wl.dtype, "forced shared pass")
