@@ -343,14 +343,17 @@ def time_decode_rotating(cfg: int, calls_per_set: int = 10):
                                                         k_pool, part)),
                      dtype=torch.uint8, device=DEV)
 
-    def call(tb):
-        pkv.decode(q, k_pool, v_pool, tb, ctx, wl.scale, max_ctx, out=out, partition=part,
-                   workspace=ws)
+    # one prepared call per block set (arguments checked and marshalled once)
+    preps = [pkv.prepare_decode(q, k_pool, v_pool, tb, ctx, wl.scale, max_ctx, out=out,
+                                partition=part, workspace=ws) for tb in tables]
+
+    def call(i):
+        preps[i]()
 
     rot = [0]
 
     def rotating():
-        call(tables[rot[0] % sets])
+        call(rot[0] % sets)
         rot[0] += 1
 
     warm_up(rotating, max(sets * 2, 200))
@@ -360,12 +363,20 @@ def time_decode_rotating(cfg: int, calls_per_set: int = 10):
     t0 = time.perf_counter()
     e0.record()
     for r in range(n):
-        call(tables[r % sets])
+        call(r % sets)
     e1.record()
     host_us = (time.perf_counter() - t0) / n * 1e6
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
     eager_out = out.clone()
+    # host time per call of the plain binding function (checks and marshalling
+    # at every call), for comparison
+    t0 = time.perf_counter()
+    for r in range(n):
+        pkv.decode(q, k_pool, v_pool, tables[r % sets], ctx, wl.scale, max_ctx, out=out,
+                   partition=part, workspace=ws)
+    host_plain_us = (time.perf_counter() - t0) / n * 1e6
+    torch.cuda.synchronize()
     loops = [ms] + [timed_loop(rotating, n) for _ in range(2)]
     # The same n calls captured in one HIP graph: replays issue no host work
     # per call, so a call shorter than the binding's host time is timed by the
@@ -373,13 +384,13 @@ def time_decode_rotating(cfg: int, calls_per_set: int = 10):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        call(tables[0])
+        call(0)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         for r in range(n):
-            call(tables[r % sets])
+            call(r % sets)
     for _ in range(3):
         graph.replay()
         torch.cuda.synchronize()
@@ -390,11 +401,11 @@ def time_decode_rotating(cfg: int, calls_per_set: int = 10):
     # when they fit: cache-assisted)
     e0.record()
     for _ in range(n):
-        call(tables[0])
+        call(0)
     e1.record()
     torch.cuda.synchronize()
     ms_warm = e0.elapsed_time(e1) / n
-    cold = time_cold(lambda: call(tables[0]))
+    cold = time_cold(lambda: call(0))
     e0.record()
     for _ in range(reps):
         graph.replay()
@@ -410,7 +421,9 @@ def time_decode_rotating(cfg: int, calls_per_set: int = 10):
             "kv_read_GBps": round(kvb / (ms * 1e-3) / 1e9, 1),
             "pct_hbm_peak": round(100 * kvb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
             "seq_steps_per_s": round(wl.num_seqs / (ms * 1e-3), 1),
+            "eager_calls": "prepared (pkv.prepare_decode: arguments marshalled once)",
             "host_issue_us_per_call": round(host_us, 2),
+            "host_issue_us_per_call_plain_binding": round(host_plain_us, 2),
             "graph_us_per_call": round(ms_graph * 1e3, 2),
             "graph_kv_read_GBps": round(kvb / (ms_graph * 1e-3) / 1e9, 1),
             "graph_pct_hbm_peak": round(100 * kvb / (ms_graph * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
@@ -485,6 +498,8 @@ def time_shared(name: str, calls_per_set: int = 20, partition: int = 0):
                    workspace=ws_p)
 
     def timed(fn):
+        """(eager ms per call, ms per call replayed from one captured graph);
+        the eager figure holds the binding's host time when a call is short."""
         for r in range(2 * sets):
             fn(tables[r % sets])
         torch.cuda.synchronize()
@@ -495,18 +510,40 @@ def time_shared(name: str, calls_per_set: int = 20, partition: int = 0):
             fn(tables[r % sets])
         e1.record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / calls
+        eager = e0.elapsed_time(e1) / calls
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn(tables[0])
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for r in range(calls):
+                fn(tables[r % sets])
+        graph.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(3):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return eager, e0.elapsed_time(e1) / (3 * calls)
 
-    ms_plain = timed(plain)
-    ms_shared = timed(shared)
+    eager_plain, ms_plain = timed(plain)
+    eager_shared, ms_shared = timed(shared)
     kv_plain = wl.kv_bytes_per_call()                 # every sequence reads its whole context
     kv_unique = (int(pl.sum()) + sum(tails)) * row_b  # each prompt once, each tail once
     return {"workload": f"{wl.name}: {len(pl)} group(s) of {mg} max, prompt {mp} tokens, "
                         f"{wl.num_seqs} seqs, {wl.num_q_heads} q / {wl.num_kv_heads} kv heads, "
                         f"head_dim {wl.head_dim}, block {wl.block_size}, {wl.dtype}",
             "rotating_sets": sets, "total_context_tokens": wl.total_ctx,
+            "timing": "graph replay (device time per call); eager_* include the binding's "
+                      "host time",
             "plain_us": round(ms_plain * 1e3, 2), "shared_us": round(ms_shared * 1e3, 2),
             "speedup": round(ms_plain / ms_shared, 3),
+            "eager_plain_us": round(eager_plain * 1e3, 2),
+            "eager_shared_us": round(eager_shared * 1e3, 2),
             "plain_kv_bytes": kv_plain, "shared_unique_kv_bytes": kv_unique,
             "plain_GBps": round(kv_plain / (ms_plain * 1e-3) / 1e9, 1),
             "shared_unique_GBps": round(kv_unique / (ms_shared * 1e-3) / 1e9, 1),

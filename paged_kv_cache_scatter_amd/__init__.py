@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     NOALLOC_SCRATCH_BYTES,
     LIB_PATH,
     PkvError,
+    PreparedCall,
     PoolDesc,
     abi_version,
     block_bytes,
@@ -24,6 +25,8 @@ from ._binding import (  # noqa: F401
     load,
     plan_pool,
     pool_desc,
+    prepare_decode,
+    prepare_decode_step,
     prefill,
     slot_mapping,
     write,

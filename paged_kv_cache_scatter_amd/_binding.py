@@ -120,8 +120,50 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
+_raw_stream_fn = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _raw_stream(device_index: int) -> int:
+    """Current stream of a device as a raw handle (the cheap path when torch has it)."""
+    if _raw_stream_fn is not None:
+        return _raw_stream_fn(device_index)
+    return torch.cuda.current_stream(device_index).cuda_stream
+
+
+class PreparedCall:
+    """One library call whose arguments were checked and converted once.
+
+    Calling it issues the same call again on the device's current stream (so it
+    can be captured into a HIP graph): the tensors it was prepared with are
+    used in place, and their contents may change between calls, but they must
+    stay alive and keep their shapes. The host cost of a call is one foreign
+    function call with pre-built arguments instead of the checks and
+    conversions of the plain functions. ``out`` is the output tensor."""
+
+    __slots__ = ("_fn", "_args", "_device", "_keep", "out")
+
+    def __init__(self, name: str, args: tuple, device: torch.device, keep: tuple, out):
+        fn = load()[name]            # a handle of its own: no per-call argument conversion
+        fn.restype = ctypes.c_int
+        self._fn = fn
+        self._args = args            # ctypes values, built once
+        self._device = device.index if device.index is not None else torch.cuda.current_device()
+        self._keep = keep            # the tensors and descriptor the pointers refer to
+        self.out = out
+
+    def __call__(self):
+        r = self._fn(*self._args, ctypes.c_void_p(_raw_stream(self._device)))
+        if r:
+            _check(r)
+        return self.out
+
+
 def _ptr(t: torch.Tensor | None) -> int | None:
     return None if t is None else t.data_ptr()
+
+
+_cp = lambda t: ctypes.c_void_p(None if t is None else t.data_ptr())
+_ci = ctypes.c_int32
 
 
 def _need(cond: bool, msg: str):
@@ -217,6 +259,16 @@ def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     buffer serves calls of any size in stream order. ``phase``: "both",
     "partials" or "reduce".
     """
+    fn, args, keep = _decode_call(q, k_pool, v_pool, block_tables, context_lens, scale,
+                                  max_context_len, out, partition, workspace, phase)
+    _check(getattr(load(), fn)(*args, _stream()))
+    return keep[-1]
+
+
+def _decode_call(q, k_pool, v_pool, block_tables, context_lens, scale, max_context_len, out,
+                 partition, workspace, phase):
+    """Checks of ``decode``; returns (entry point, typed arguments without the
+    stream, tensors they point to with ``out`` last)."""
     desc = _check_pools(k_pool, v_pool)
     _dev(q, "q", k_pool.dtype)
     _need(q.dim() == 3 and q.shape[2] == desc.head_dim, "q must be [S, Hq, head_dim]")
@@ -239,11 +291,22 @@ def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
         ws_bytes = workspace.numel()
     fn = {"both": "pkv_decode", "partials": "pkv_decode_partials",
           "reduce": "pkv_decode_reduce"}[phase]
-    _check(getattr(load(), fn)(_ptr(q), S, Hq, _ptr(k_pool), _ptr(v_pool), ctypes.byref(desc),
-                               _ptr(block_tables), maxb, _ptr(context_lens),
-                               int(max_context_len), float(scale), int(partition), _ptr(out),
-                               _ptr(workspace), ws_bytes, _stream()))
-    return out
+    args = (_cp(q), _ci(S), _ci(Hq), _cp(k_pool), _cp(v_pool), ctypes.byref(desc),
+            _cp(block_tables), _ci(maxb), _cp(context_lens), _ci(int(max_context_len)),
+            ctypes.c_float(float(scale)), _ci(int(partition)), _cp(out), _cp(workspace),
+            ctypes.c_size_t(ws_bytes))
+    return fn, args, (desc, q, k_pool, v_pool, block_tables, context_lens, workspace, out)
+
+
+def prepare_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                   block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                   max_context_len: int, out: torch.Tensor | None = None, partition: int = 0,
+                   workspace: torch.Tensor | None = None) -> PreparedCall:
+    """``decode`` checked and marshalled once: returns a PreparedCall that
+    launches the same decode on the current stream each time it is called."""
+    fn, args, keep = _decode_call(q, k_pool, v_pool, block_tables, context_lens, scale,
+                                  max_context_len, out, partition, workspace, "both")
+    return PreparedCall(fn, args, q.device, keep, keep[-1])
 
 
 def decode_shared_workspace_bytes(num_seqs: int, num_q_heads: int, max_context_len: int,
@@ -313,6 +376,16 @@ def decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
     their slots and attended. ``workspace`` as for ``decode`` (zero-filled
     before its first use). ``phase``: "both", "partials" (then call
     ``decode(..., phase="reduce")`` with the same arguments) or "reduce"."""
+    fn, args, keep = _step_call(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens,
+                                scale, max_context_len, out, partition, workspace, phase)
+    _check(getattr(load(), fn)(*args, _stream()))
+    return keep[-1]
+
+
+def _step_call(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale,
+               max_context_len, out, partition, workspace, phase):
+    """Checks of ``decode_step``; returns (entry point, typed arguments without
+    the stream, tensors they point to with ``out`` last)."""
     desc = _check_pools(k_pool, v_pool)
     _dev(q, "q", k_pool.dtype)
     _need(q.dim() == 3 and q.shape[2] == desc.head_dim, "q must be [S, Hq, head_dim]")
@@ -335,17 +408,29 @@ def decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
     if workspace is not None:
         _dev(workspace, "workspace", torch.uint8)
         ws_bytes = workspace.numel()
-    lib = load()
-    common = (ctypes.byref(desc), _ptr(block_tables), maxb, _ptr(context_lens),
-              int(max_context_len), float(scale), int(partition), _ptr(out), _ptr(workspace),
-              ws_bytes, _stream())
+    _need(phase in ("both", "partials", "reduce"), f"unknown phase {phase!r}")
+    common = (ctypes.byref(desc), _cp(block_tables), _ci(maxb), _cp(context_lens),
+              _ci(int(max_context_len)), ctypes.c_float(float(scale)), _ci(int(partition)),
+              _cp(out), _cp(workspace), ctypes.c_size_t(ws_bytes))
+    keep = (desc, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, workspace, out)
     if phase == "reduce":
-        _check(lib.pkv_decode_reduce(_ptr(q), S, Hq, _ptr(k_pool), _ptr(v_pool), *common))
-    else:
-        fn = lib.pkv_decode_step if phase == "both" else lib.pkv_decode_step_partials
-        _need(phase in ("both", "partials"), f"unknown phase {phase!r}")
-        _check(fn(_ptr(q), _ptr(k_new), _ptr(v_new), S, Hq, _ptr(k_pool), _ptr(v_pool), *common))
-    return out
+        return "pkv_decode_reduce", (_cp(q), _ci(S), _ci(Hq), _cp(k_pool), _cp(v_pool)) + common, \
+            keep
+    fn = "pkv_decode_step" if phase == "both" else "pkv_decode_step_partials"
+    return fn, (_cp(q), _cp(k_new), _cp(v_new), _ci(S), _ci(Hq), _cp(k_pool), _cp(v_pool)) + \
+        common, keep
+
+
+def prepare_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                        k_pool: torch.Tensor, v_pool: torch.Tensor, block_tables: torch.Tensor,
+                        context_lens: torch.Tensor, scale: float, max_context_len: int,
+                        out: torch.Tensor | None = None, partition: int = 0,
+                        workspace: torch.Tensor | None = None) -> PreparedCall:
+    """``decode_step`` checked and marshalled once: returns a PreparedCall that
+    launches the same fused step on the current stream each time it is called."""
+    fn, args, keep = _step_call(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens,
+                                scale, max_context_len, out, partition, workspace, "both")
+    return PreparedCall(fn, args, q.device, keep, keep[-1])
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20   # PKV_NOALLOC_SCRATCH_BYTES of include/pkv.h
