@@ -749,6 +749,109 @@ def cpu_pages_plan_baseline(wl, budget_s: float = 6.0):
             "seq_steps_per_s": round(seqs / wall, 3)}
 
 
+TRACE_LIB = os.path.join(ROOT, "paged_kv_cache_scatter_amd", "libpkv_trace.so")
+PHASES = ["entry", "piece and context length known", "queries and block ids arrived",
+          "first K/V tile in LDS", "tiles done", "partial stored", "stores acknowledged",
+          "counted", "end"]
+
+
+def phase_trace(cfg: int):
+    """One launch of the decode (config 5: the fused step) through the traced
+    build (libpkv_trace.so: the same kernels recording the 100 MHz realtime
+    counter at each phase boundary of every workgroup), after warm-up and a
+    512 MiB cache-evicting write. Returns per-phase durations over the
+    workgroups, the launch's timeline and how many workgroups are alive over
+    it. The traced kernel waits for each timestamp, so it runs a little slower
+    than the normal build."""
+    import ctypes
+    from paged_kv_cache_scatter_amd._binding import PoolDesc
+    if not os.path.exists(TRACE_LIB):
+        raise SystemExit(f"{TRACE_LIB} is not built; run __graft_entry__.build()")
+    L = ctypes.CDLL(TRACE_LIB)
+    P, I = ctypes.c_void_p, ctypes.c_int32
+    L.pkv_decode_step.argtypes = [P, P, P, I, I, P, P, ctypes.POINTER(PoolDesc), P, I, P, I,
+                                  ctypes.c_float, I, P, P, ctypes.c_size_t, P]
+    L.pkv_decode.argtypes = [P, I, I, P, P, ctypes.POINTER(PoolDesc), P, I, P, I,
+                             ctypes.c_float, I, P, P, ctypes.c_size_t, P]
+    L.pkv_decode_workspace_bytes.argtypes = [I, I, I, I, ctypes.POINTER(PoolDesc)]
+    L.pkv_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.pkv_decode_partition.argtypes = [I, I, ctypes.POINTER(PoolDesc)]
+    L.pkv_phase_trace_clear.argtypes = [P, ctypes.c_size_t]
+    L.pkv_phase_trace_copy.argtypes = [P, ctypes.c_size_t]
+    wl = make_workload(cfg)
+    st = Step(wl)
+    desc = pkv.pool_desc(st.k_pool)
+    part = L.pkv_decode_partition(wl.num_seqs, st.max_ctx, ctypes.byref(desc))
+    ws = torch.zeros(max(16, L.pkv_decode_workspace_bytes(wl.num_seqs, wl.num_q_heads,
+                                                          st.max_ctx, part, ctypes.byref(desc))),
+                     dtype=torch.uint8, device=DEV)
+    fused = cfg == 5
+
+    def call():
+        strm = torch.cuda.current_stream().cuda_stream
+        if fused:
+            r = L.pkv_decode_step(st.q.data_ptr(), st.k_step.data_ptr(), st.v_step.data_ptr(),
+                                  wl.num_seqs, wl.num_q_heads, st.k_pool.data_ptr(),
+                                  st.v_pool.data_ptr(), ctypes.byref(desc), st.tables.data_ptr(),
+                                  wl.block_tables.shape[1], st.ctx.data_ptr(), st.max_ctx,
+                                  wl.scale, part, st.out.data_ptr(), ws.data_ptr(), ws.numel(),
+                                  strm)
+        else:
+            r = L.pkv_decode(st.q.data_ptr(), wl.num_seqs, wl.num_q_heads, st.k_pool.data_ptr(),
+                             st.v_pool.data_ptr(), ctypes.byref(desc), st.tables.data_ptr(),
+                             wl.block_tables.shape[1], st.ctx.data_ptr(), st.max_ctx, wl.scale,
+                             part, st.out.data_ptr(), ws.data_ptr(), ws.numel(), strm)
+        if r:
+            raise SystemExit(f"traced call failed with status {r}")
+
+    warm_up(call, 200)
+    rows, cols = 1 << 16, 10
+    buf = np.zeros((rows, cols), dtype=np.uint64)
+    scratch = torch.empty(COLD_FLUSH_BYTES, dtype=torch.uint8, device=DEV)
+    scratch.fill_(1)
+    torch.cuda.synchronize()
+    if L.pkv_phase_trace_clear(buf.ctypes.data, buf.nbytes):
+        raise SystemExit("clearing the phase trace failed")
+    call()
+    torch.cuda.synchronize()
+    if L.pkv_phase_trace_copy(buf.ctypes.data, buf.nbytes):
+        raise SystemExit("copying the phase trace failed")
+    del scratch
+    t = buf.astype(np.int64)
+    t = t[(t[:, 0] > 0) & (t[:, 8] > 0)]
+    us = lambda ticks: ticks / 100.0            # 100 MHz counter
+    phases = {}
+    for i in range(8):
+        a, b = t[:, i], t[:, i + 1]
+        ok = (a > 0) & (b > 0)
+        d = us(b[ok] - a[ok])
+        if ok.any():
+            phases[f"{PHASES[i]} -> {PHASES[i + 1]}"] = {
+                "workgroups": int(ok.sum()), "mean_us": round(float(d.mean()), 2),
+                "p50_us": round(float(np.median(d)), 2),
+                "p90_us": round(float(np.percentile(d, 90)), 2)}
+    start = us(t[:, 0] - t[:, 0].min())
+    end = us(t[:, 8] - t[:, 0].min())
+    first = us(t[:, 3] - t[:, 0].min())
+    step_us = 2.0 if end.max() < 60 else 5.0
+    bins = np.arange(0.0, end.max() + step_us, step_us)
+    merged = t[:, 9] == 1
+    return {"workload": workload_label(wl), "call": "pkv_decode_step" if fused else "pkv_decode",
+            "partition": part, "workgroups": int(len(t)), "phases": phases,
+            "workgroup_total_us": {"mean": round(float((end - start).mean()), 2),
+                                   "p50": round(float(np.median(end - start)), 2),
+                                   "p90": round(float(np.percentile(end - start, 90)), 2)},
+            "last_start_us": round(float(start.max()), 2),
+            "last_end_us": round(float(end.max()), 2),
+            "first_kv_in_lds_us": {"min": round(float(first.min()), 2),
+                                   "p50": round(float(np.median(first)), 2)},
+            "merging_workgroups": int(merged.sum()),
+            "merge_us_mean": round(float(us(t[merged, 8] - t[merged, 7]).mean()), 2)
+            if merged.any() else None,
+            "alive_bin_us": step_us,
+            "alive": [int(((start <= b) & (end > b)).sum()) for b in bins]}
+
+
 def traffic_from_counters(kernel_src: str):
     """HBM bytes per launch measured by rocprofv3 counters, if they were taken on
     the current kernel source; else None."""
@@ -843,10 +946,20 @@ def main():
     ap.add_argument("--layer-graph", nargs="+", type=int, metavar="CFG",
                     help="only time a 16-layer decode step of these configs, layer by layer "
                          "and replayed from one captured HIP graph")
+    ap.add_argument("--phase-trace", nargs="+", type=int, metavar="CFG",
+                    help="only per-workgroup phase timings of one decode launch of these "
+                         "configs, from the traced build (libpkv_trace.so)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the chunked-prefill leg, two calls after one warm-up (for "
                          "counter runs)")
     args = ap.parse_args()
+    if args.phase_trace:
+        pkv.load()
+        for cfg in args.phase_trace:
+            print(f"[bench] phase trace, {CONFIGS[cfg].name}", file=sys.stderr, flush=True)
+            print(json.dumps({"phase_trace": phase_trace(cfg)}), flush=True)
+            torch.cuda.empty_cache()
+        return
     if args.prefill_only:
         pkv.load()
         step = Step(make_workload(args.config), args.partition)

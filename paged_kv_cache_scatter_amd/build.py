@@ -2,7 +2,8 @@
 
 Every source is compiled to an object in parallel, then linked in-tree into
 ``paged_kv_cache_scatter_amd/libpkv.so``; the benchmark's read-bandwidth
-probes go into ``libpkv_probe.so`` beside it. Run as ``python -m
+probes go into ``libpkv_probe.so`` beside it, and a copy of the library whose
+decode kernel records phase timestamps into ``libpkv_trace.so``. Run as ``python -m
 paged_kv_cache_scatter_amd.build``.
 """
 
@@ -22,6 +23,9 @@ HOST_SOURCES = ["pkv_sched.cpp"]   # host-only C++ (the scheduler above the kern
 # read-bandwidth probes for the benchmark, in a library of their own
 PROBE_SOURCE = "pkv_probe.hip"
 PROBE_LIB = os.path.join(PKG, "libpkv_probe.so")
+# the same library with the decode kernel's phase timestamps compiled in
+# (PKV_PHASE_TRACE), for the benchmark's --phase-trace
+TRACE_LIB = os.path.join(PKG, "libpkv_trace.so")
 ARCH = "gfx950"
 
 # Packed-fp32 VALU ops are switched off for the device code; hipcc's host pass
@@ -70,6 +74,9 @@ def build(verbose: bool = False) -> str:
         objs.append(o)
     probe_tmp = PROBE_LIB + ".tmp"
     cmds.append([cc, *FLAGS, "-shared", os.path.join(CSRC, PROBE_SOURCE), "-o", probe_tmp])
+    trace_obj = os.path.join(objdir, "pkv_decode_trace.o")
+    cmds.append([cc, *FLAGS, "-DPKV_PHASE_TRACE", "-c", os.path.join(CSRC, "pkv_decode.hip"),
+                 "-o", trace_obj])
     workers = min(len(cmds), max(1, (os.cpu_count() or 4)))
     with ThreadPoolExecutor(max_workers=workers) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
@@ -77,6 +84,10 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    trace_objs = [trace_obj if o.endswith("pkv_decode.o") else o for o in objs]
+    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *trace_objs, "-o", TRACE_LIB + ".tmp"],
+         verbose)
+    os.replace(TRACE_LIB + ".tmp", TRACE_LIB)
     return LIB
 
 

@@ -42,6 +42,35 @@ namespace {
 
 using namespace dev;
 
+// Phase timestamps (the benchmark's traced build, libpkv_trace.so, compiled
+// with PKV_PHASE_TRACE): wave 0 of each workgroup records the 100 MHz
+// realtime counter at the phase boundaries of the decode kernel into one row
+// per linear workgroup id. Phases: 0 entry, 1 piece and context length known,
+// 2 queries and block ids arrived, 3 first K/V tile in LDS, 4 tiles done,
+// 5 partial stored, 6 stores acknowledged, 7 counted, 8 end; slot 9 is 1 for
+// the workgroup that merged. The normal build compiles all of this away.
+#ifdef PKV_PHASE_TRACE
+constexpr int kTraceRows = 1 << 16, kTraceCols = 10;
+__device__ unsigned long long g_phase_trace[kTraceRows][kTraceCols];
+__device__ __forceinline__ unsigned long long phase_clock() {
+  unsigned long long t;
+  asm volatile("s_memrealtime %0\n\ts_waitcnt lgkmcnt(0)" : "=s"(t) :: "memory");
+  return t;
+}
+__device__ __forceinline__ void phase_set(int i, unsigned long long v) {
+  // a wave-uniform condition, so that no scalar value becomes divergent
+  if (__builtin_amdgcn_readfirstlane(threadIdx.x) < 64) {
+    const int w = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    if (w < kTraceRows) g_phase_trace[w][i] = v;
+  }
+}
+#define PKV_PHASE(i) phase_set((i), phase_clock())
+#define PKV_PHASE_VALUE(i, v) phase_set((i), (unsigned long long)(v))
+#else
+#define PKV_PHASE(i) do { } while (0)
+#define PKV_PHASE_VALUE(i, v) do { } while (0)
+#endif
+
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 
@@ -640,6 +669,7 @@ __device__ __forceinline__ void wave_tiles(const SplitCtx& c, const Lanes& ln,
   // compiler puts no waits for them inside the loop (where they would also
   // stall on the ring's loads).
   __builtin_amdgcn_s_waitcnt(0);
+  PKV_PHASE(2);
   TI ti[S];
 #pragma unroll
   for (int q = 0; q < S - 1; ++q) {
@@ -662,6 +692,7 @@ __device__ __forceinline__ void wave_tiles(const SplitCtx& c, const Lanes& ln,
     } else {
       wait_tiles_after<G::LOADS, S>(n - 1 - k);
     }
+    if (k == 0) PKV_PHASE(3);
     compute_tile<T, HD, REP, UNI, PR>(c, ln, st, qr, tb0 + k * kStep, ti[0],
                                       ring + (k % S) * G::STAGE, pbuf, cbuf);
 #pragma unroll
@@ -1006,6 +1037,7 @@ decode_partials_kernel(DecodeArgs a) {
   // Splits are dispatched last-index first: the later splits exist only for
   // the longer sequences, so their work starts early and the tail of the
   // launch is made of the short first splits.
+  PKV_PHASE(0);
   const int g = blockIdx.x;
   int s = blockIdx.y, j = gridDim.z - 1 - blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1071,6 +1103,7 @@ decode_partials_kernel(DecodeArgs a) {
   const int hq0 = g * REP;
   T* out = reinterpret_cast<T*>(a.out) + ((size_t)qrow * a.num_q_heads + hq0) * QHD;
 
+  PKV_PHASE(1);
   if (sched ? ctx == 0 : j >= nsplit) {
     if (j == 0 && nps == 0) {  // empty sequence: zeros
       for (int i = tid; i < REP * QHD; i += kThreads) out[i] = from_f32<T>(0.f);
@@ -1202,6 +1235,7 @@ decode_partials_kernel(DecodeArgs a) {
                                                ring);
   }
 
+  PKV_PHASE(4);
   // ---- per-wave totals, then merge the waves in LDS
   float* mw = merge + w * L::kMergeFloats;
 #pragma unroll
@@ -1266,7 +1300,14 @@ decode_partials_kernel(DecodeArgs a) {
       }
     }
   }
-  if (!a.counters || (nsplit == 1 && nps == 0)) return;
+  PKV_PHASE(5);
+  if (!a.counters || (nsplit == 1 && nps == 0)) {
+#ifdef PKV_PHASE_TRACE
+    wait_vmcnt<0>();
+    PKV_PHASE(8);
+#endif
+    return;
+  }
 
   // ---- in-launch merge: the last workgroup of (s, g) to count itself merges.
   // Each wave waits until its device-coherent partial stores are complete
@@ -1293,6 +1334,7 @@ decode_partials_kernel(DecodeArgs a) {
   wait_vmcnt<0>();
   int* last = reinterpret_cast<int*>(smem) + kWaves * 64;
   __syncthreads();
+  PKV_PHASE(6);
   if (nsplit > 1) {
     if (tid == 0) {
       int* cnt = a.counters + (size_t)s * a.num_kv_heads + g;
@@ -1302,10 +1344,20 @@ decode_partials_kernel(DecodeArgs a) {
       if (before == nsplit - 1) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
-    if (!*last) return;
+    PKV_PHASE(7);
+    PKV_PHASE_VALUE(9, *last);
+    if (!*last) {
+      PKV_PHASE(8);
+      return;
+    }
   }
   merge_partials<T, HD, REP, PR>(a, s, hq0, nps, slot0, nsplit, out,
                              reinterpret_cast<float*>(smem) + w * 64, w, lane);
+#ifdef PKV_PHASE_TRACE
+  wait_vmcnt<0>();
+  __syncthreads();
+  PKV_PHASE(8);
+#endif
 }
 
 // Merge split partials of sequences with more than one split: one wave per
@@ -1460,3 +1512,16 @@ pkv_status launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hi
 }
 
 }  // namespace pkv
+
+#ifdef PKV_PHASE_TRACE
+// The traced build's access to the timestamps (host memory, kTraceRows x
+// kTraceCols uint64): clear before a call, copy after it has completed.
+extern "C" int pkv_phase_trace_clear(const void* zeros, size_t bytes) {
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(pkv::g_phase_trace), zeros, bytes, 0,
+                                hipMemcpyHostToDevice);
+}
+extern "C" int pkv_phase_trace_copy(void* host, size_t bytes) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(pkv::g_phase_trace), bytes, 0,
+                                  hipMemcpyDeviceToHost);
+}
+#endif
