@@ -209,12 +209,21 @@ __device__ __forceinline__ void attend_rows(const PrefillArgs& a, const Work& wk
     dc[i] = ((o % G::ROWB) >> 4) ^ swz<T, HD>(dr[i]);   // logical chunk to fetch
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  auto issue = [&](int t) {
+  // block id of each of the lane's rows of tile t (-1 past the keys or for an
+  // invalid entry), read from LDS a tile before its loads are issued
+  auto ids = [&](int t, int (&b)[G::LOADS]) {
+#pragma unroll
+    for (int i = 0; i < G::LOADS; ++i) {
+      const int key = key_lo + t * KT + dr[i];
+      b[i] = key < key_hi ? tbl[(key >> bshift) - tb0] : -1;
+    }
+  };
+  auto issue = [&](int t, const int (&bid)[G::LOADS]) {
     const uint32_t kdst = lds0 + (t & 1) * G::STAGE + w * G::LOADS * 1024;
 #pragma unroll
     for (int i = 0; i < G::LOADS; ++i) {
       const int key = key_lo + t * KT + dr[i];
-      const int b = key < key_hi ? tbl[(key >> bshift) - tb0] : -1;
+      const int b = bid[i];
       const char* kp;
       const char* vp;
       if (b >= 0) {
@@ -244,11 +253,17 @@ __device__ __forceinline__ void attend_rows(const PrefillArgs& a, const Work& wk
 
   const int ntiles = (key_hi - key_lo + KT - 1) / KT;
   __builtin_amdgcn_s_waitcnt(0);   // q fragments and table reads are in
-  issue(0);
+  int bnext[G::LOADS];
+  ids(0, bnext);
+  issue(0, bnext);
+  if (ntiles > 1) ids(1, bnext);
   for (int t = 0; t < ntiles; ++t) {
     wait_vmcnt<0>();
     __syncthreads();   // tile t is in LDS; tile t-1's stage is free
-    if (t + 1 < ntiles) issue(t + 1);
+    if (t + 1 < ntiles) {
+      issue(t + 1, bnext);
+      if (t + 2 < ntiles) ids(t + 2, bnext);   // consumed at the next issue
+    }
 
     const unsigned char* kt = smem + (t & 1) * G::STAGE;
     const unsigned char* vt = kt + G::TILEB;
@@ -289,11 +304,14 @@ __device__ __forceinline__ void attend_rows(const PrefillArgs& a, const Work& wk
           sc[kb][nb][i] = v;
           mx = fmaxf(mx, v);
         }
-      mx = fmaxf(mx, swz_xor16(mx));
-      mx = fmaxf(mx, xor32(mx));
+      // the row's 16 lanes of each of the four lane groups: join the groups
+      // with VALU cross-lane swaps (lanes i ^ 16, then i ^ 32)
+      mx = join16<true>(mx);
+      mx = join32<true>(mx);
       const float mn = fmaxf(m[nb], mx);
       const float mu = mn == -INFINITY ? 0.f : mn;
       const float alpha = fast_exp2(m[nb] - mu);
+      const bool moved = __any(mn > m[nb]);
       m[nb] = mn;
       float sum = 0.f;
 #pragma unroll
@@ -309,8 +327,12 @@ __device__ __forceinline__ void attend_rows(const PrefillArgs& a, const Work& wk
         sc[3][nb][i] = e3;
       }
       lsum[nb] = lsum[nb] * alpha + sum;
+      // no row's max moved: alpha is 1 everywhere and o needs no rescale
+      // (nor does the next product have to wait for o's previous value)
+      if (moved) {
 #pragma unroll
-      for (int d = 0; d < G::DB; ++d) o[d][nb] *= alpha;
+        for (int d = 0; d < G::DB; ++d) o[d][nb] *= alpha;
+      }
     }
 
     if constexpr (G::ISZ == 2) {
@@ -375,8 +397,8 @@ __device__ __forceinline__ void attend_rows(const PrefillArgs& a, const Work& wk
 #pragma unroll
   for (int nb = 0; nb < NBLK; ++nb) {
     float tot = lsum[nb];
-    tot += swz_xor16(tot);
-    tot += xor32(tot);
+    tot = join16<false>(tot);
+    tot = join32<false>(tot);
     if constexpr (SHARED) {
       // split partial: running max (log2 units), exp-sum, unnormalised o
       if (!emit[nb]) continue;
