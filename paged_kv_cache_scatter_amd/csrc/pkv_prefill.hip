@@ -33,8 +33,14 @@
 //                   the order the score layout produced them (the same
 //                   permutation on both operands leaves the sum unchanged).
 // K/V tiles are filled by global_load_lds_dwordx4 (double-buffered, one
-// barrier per tile), with a per-row XOR swizzle of 16-byte chunks so that the
-// 16-row K reads and the V reads hit distinct LDS banks. Keys past the last
+// barrier per tile), with a per-row XOR swizzle of 16-byte chunks (below).
+// Measured LDS read rates on gfx950 (bytes per clock per CU, 8 or more waves):
+// the bf16 swizzle gives the transposing V reads 225-239 (conflict-free) but
+// the 16-row K reads only 128, a 2-way bank conflict; swizzling K by r & 15
+// instead gives K 231 and V 128. A layout with separate K and V swizzles,
+// conflict-free on both, ran the chunked prefill in the same time, so the
+// conflicts are not what bounds this kernel and the single layout is kept.
+// Keys past the last
 // visible one, and keys of invalid table entries, are loaded from a zero row
 // and masked, so masked V rows contribute exactly 0. Workgroups are numbered
 // so that all tiles of one (sequence or group, KV head) run on one XCD and
@@ -92,11 +98,15 @@ struct MG {
 };
 
 // Physical 16-byte chunk of logical chunk c in tile row r is c ^ swz(r).
-// bf16: for the 16 rows a K read touches the chunks are distinct, and for the
-// 8 rows of each half-wave of a transposing V read (two adjacent logical
-// chunks) the 16 chunks are too. fp32: the 16 rows of a K read get distinct
-// chunks modulo 16 (one 256-byte bank line), and the four rows r, r+4, r+8,
-// r+12 of a V read get disjoint 64-byte quarters of the line.
+// bf16: the 16 rows a K read touches get distinct chunks, and so do the 8 rows
+// of each half-wave of a transposing V read (two adjacent logical chunks).
+// Distinct chunks are not enough for the K reads on gfx950: a 16-byte read is
+// conflict-free only when each group of 8 lanes also spreads over distinct
+// 16-byte slots of a 128-byte half line, which this mapping does not give (K
+// reads run 2-way conflicted; the V reads are conflict-free). fp32: the 16
+// rows of a K read get distinct chunks modulo 16 (one 256-byte bank line), and
+// the four rows r, r+4, r+8, r+12 of a V read get disjoint 64-byte quarters of
+// the line.
 template <typename T, int HD>
 __device__ __forceinline__ int swz(int r) {
   using G = MG<T, HD>;
