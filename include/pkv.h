@@ -368,7 +368,8 @@ pkv_status pkv_prefill(const void* q, const int32_t* cu_q, int32_t num_seqs,
  * pkv_block_bytes: bytes of one block of a layered pool, K and V for every
  * layer and KV head: 2 * num_layers * block_size * num_kv_heads * head_dim *
  * itemsize (512 KiB for Llama-3.2-1B at block 16 in bf16; use the KV head
- * count, not the attention head count). Returns 0 if an argument is < 1.
+ * count, not the attention head count). Returns 0 if an argument is < 1 and
+ * -1 (pkv_last_error() says why) if the product does not fit in int64.
  *
  * pkv_plan_pool: the number of blocks a device holds after the weights are
  * resident,

@@ -84,8 +84,9 @@ pkv_status pkv_sched_submit(pkv_sched* s, int32_t rid, int32_t prompt_len, int32
 /* Requests waiting or running. */
 int32_t pkv_sched_pending(const pkv_sched* s);
 
-/* One engine step. PKV_ERR_CAPACITY if nothing can run and nothing fits
- * (a request larger than the whole pool). */
+/* One engine step. PKV_ERR_NULL if s, out or one of out's arrays is NULL
+ * (nothing changes then); PKV_ERR_CAPACITY if nothing can run and nothing
+ * fits (a request larger than the whole pool). */
 pkv_status pkv_sched_step(pkv_sched* s, pkv_sched_step_out* out);
 
 pkv_status pkv_sched_get_stats(const pkv_sched* s, pkv_sched_stats* st);

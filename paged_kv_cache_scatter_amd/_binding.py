@@ -494,9 +494,13 @@ def abi_version() -> int:
 # ---------------------------------------------------------------- pool sizing
 def block_bytes(num_layers: int, block_size: int, num_kv_heads: int, head_dim: int,
                 itemsize: int) -> int:
-    """Bytes of one block of a layered K/V pool (0 if an argument is < 1)."""
-    return int(load().pkv_block_bytes(int(num_layers), int(block_size), int(num_kv_heads),
-                                      int(head_dim), int(itemsize)))
+    """Bytes of one block of a layered K/V pool (0 if an argument is < 1);
+    raises PkvError if the size does not fit in int64."""
+    n = int(load().pkv_block_bytes(int(num_layers), int(block_size), int(num_kv_heads),
+                                   int(head_dim), int(itemsize)))
+    if n < 0:
+        raise PkvError(3, load().pkv_last_error().decode())   # PKV_ERR_SHAPE
+    return n
 
 
 def plan_pool(free_bytes: int, total_bytes: int, utilization: float, activation_bytes: int,

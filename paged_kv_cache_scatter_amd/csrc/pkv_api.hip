@@ -821,7 +821,14 @@ int64_t pkv_block_bytes(int32_t num_layers, int32_t block_size, int32_t num_kv_h
                         int32_t head_dim, int32_t itemsize) {
   if (num_layers < 1 || block_size < 1 || num_kv_heads < 1 || head_dim < 1 || itemsize < 1)
     return 0;
-  return (int64_t)2 * num_layers * block_size * num_kv_heads * head_dim * itemsize;
+  int64_t bytes = 2;
+  for (const int32_t f : {num_layers, block_size, num_kv_heads, head_dim, itemsize})
+    if (__builtin_mul_overflow(bytes, (int64_t)f, &bytes)) {
+      set_error("block bytes 2 * %d * %d * %d * %d * %d exceed int64", num_layers, block_size,
+                num_kv_heads, head_dim, itemsize);
+      return -1;
+    }
+  return bytes;
 }
 
 pkv_status pkv_plan_pool(int64_t free_bytes, int64_t total_bytes, double utilization,
@@ -843,7 +850,8 @@ pkv_status pkv_plan_pool(int64_t free_bytes, int64_t total_bytes, double utiliza
   // reserve = (1 - utilization) * total, rounded up to whole bytes
   const long double reserve = (1.0L - (long double)utilization) * (long double)total_bytes;
   const long double budget = (long double)free_bytes - reserve - (long double)activation_bytes;
-  const int64_t blocks = budget > 0 ? (int64_t)(budget / (long double)block_bytes) : 0;
+  const long double q = budget > 0 ? budget / (long double)block_bytes : 0.0L;
+  const int64_t blocks = q >= (long double)INT64_MAX ? INT64_MAX : (int64_t)q;
   const int64_t per_req = ((int64_t)max_model_len + block_size - 1) / block_size;
   *num_blocks = blocks;
   *requests_at_max_len = per_req > 0 ? blocks / per_req : 0;

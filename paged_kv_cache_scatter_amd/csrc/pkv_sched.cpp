@@ -170,6 +170,11 @@ pkv_status pkv_sched_step(pkv_sched* s, pkv_sched_step_out* out) {
     pkv::set_error("scheduler or output is NULL");
     return PKV_ERR_NULL;
   }
+  if (!out->prefill_rid || !out->prefill_len || !out->prefill_tables || !out->decode_rid ||
+      !out->decode_pos || !out->decode_tables) {
+    pkv::set_error("an output array of the step is NULL");
+    return PKV_ERR_NULL;
+  }
   out->num_prefill = out->num_decode = out->num_preempted = out->num_finished = 0;
   const int64_t pre0 = s->stats.preemptions;
   for (auto& r : s->running) r.fresh = false;

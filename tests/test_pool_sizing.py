@@ -76,3 +76,14 @@ def test_bad_arguments():
     # a budget that goes negative is an empty pool, refused for any request
     with pytest.raises(pkv.PkvError):
         pkv.plan_pool(GIB, 24 * GIB, 0.5, 0, 512 * KIB, 16, 16)
+
+
+def test_block_bytes_past_int64_is_an_error():
+    # 2 * (2^31 - 1)^3 * 8 bytes does not fit in int64: refused, not wrapped
+    big = 2**31 - 1
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.block_bytes(big, big, big, 128, 8)
+    assert e.value.status_name == "PKV_ERR_SHAPE" and "exceed int64" in str(e.value)
+    # the largest sizes that fit still give the exact product
+    assert pkv.block_bytes(2**15, 256, 2**10, 2**10, 4) == 2 * 2**15 * 256 * 2**10 * 2**10 * 4
+    assert pkv.block_bytes(0, 16, 8, 128, 2) == 0
