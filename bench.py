@@ -499,10 +499,16 @@ def time_shared(name: str, calls_per_set: int = 20, partition: int = 0):
 
     def timed(fn):
         """(eager ms per call, ms per call replayed from one captured graph);
-        the eager figure holds the binding's host time when a call is short."""
-        for r in range(2 * sets):
-            fn(tables[r % sets])
-        torch.cuda.synchronize()
+        the eager figure holds the binding's host time when a call is short.
+        Both follow the same minimum-time warm-up as the other legs, so the
+        first series timed in the process is not the slow one."""
+        rot = [0]
+
+        def rotating():
+            fn(tables[rot[0] % sets])
+            rot[0] += 1
+
+        warm_up(rotating, 2 * sets)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         calls = sets * calls_per_set
         e0.record()
