@@ -363,6 +363,43 @@ pkv_status pkv_prefill(const void* q, const int32_t* cu_q, int32_t num_seqs,
                        void* stream);
 
 /* ---------------------------------------------------------------------------
+ * pkv_validate -- debug check of the index data a write or a decode uses.
+ * The path's kernels never check device indices against each other (that
+ * would need a synchronisation): a write skips slots outside the pool and
+ * keeps one of several rows sent to one slot, a decode or prefill leaves the
+ * tokens of an invalid table entry out of the softmax and clamps a context to
+ * the table's reach. Each token is written once ([MV] section 4) and a table
+ * maps a sequence's blocks into the pool ([NV] "How it works"), so any of
+ * these is a caller error this call makes visible. It writes five int32
+ * counters to report (device memory, overwritten):
+ *   report[0]  slots < 0 (pkv_slot_mapping gives -1 for a position past the
+ *              table or through an invalid entry; padding rows may use it)
+ *   report[1]  slots >= num_blocks * block_size
+ *   report[2]  duplicate slots: tokens of this call whose slot another token
+ *              also names (k tokens on one slot count k - 1)
+ *   report[3]  table entries outside [0, num_blocks) among the blocks
+ *              0 .. ceil(ctx / block_size) - 1 a sequence needs
+ *   report[4]  context lengths < 0 or > max_blocks_per_seq * block_size
+ * Slots are checked when slot_mapping is non-NULL and num_tokens > 0; tables
+ * when block_tables is non-NULL and num_seqs > 0 (context_lens is then
+ * required). Checking slots needs `workspace`: pkv_validate_workspace_bytes()
+ * bytes (one bit per pool slot), 4-byte aligned, zero on entry; the call
+ * leaves it zero again, so one buffer serves every call in stream order.
+ * Device pointers: slot_mapping, block_tables, context_lens, workspace,
+ * report. Up to four launches on `stream`, nothing allocated; read report
+ * after synchronising. Errors: PKV_ERR_NULL (report, or context_lens when
+ * tables are checked), PKV_ERR_SHAPE, PKV_ERR_UNSUPPORTED (block size),
+ * PKV_ERR_WORKSPACE.
+ * ------------------------------------------------------------------------- */
+size_t pkv_validate_workspace_bytes(int32_t num_blocks, int32_t block_size);
+
+pkv_status pkv_validate(const int32_t* slot_mapping, int32_t num_tokens,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        const int32_t* context_lens, int32_t num_seqs, int32_t num_blocks,
+                        int32_t block_size, void* workspace, size_t workspace_bytes,
+                        int32_t* report, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Pool sizing ([D38] "Why it matters"; host arithmetic, no device access).
  *
  * pkv_block_bytes: bytes of one block of a layered pool, K and V for every

@@ -11,6 +11,7 @@ from .pkv_oracle import (  # noqa: F401
     combine_partials,
     decode,
     decode_one,
+    index_errors,
     prefill,
     prefill_one,
     slot_mapping,

@@ -23,6 +23,11 @@ What it computes, and where the pages define it:
   with the dummy block 0, which is never read ("nano-vLLM", "How it works").
   Here the rows are looked up position by position and each query head's
   softmax is computed on its own; the result is the same definition.
+* Index errors (for the debug check) -- counts of negative, past-the-pool and
+  duplicate slots of one write, of table entries outside the pool among the
+  blocks a sequence needs, and of context lengths outside the table's reach
+  (each token is written once: "Build a Mini vLLM", section 4; tables name
+  pool blocks: "nano-vLLM", "How it works").
 * Causal prefill -- "Build a Mini vLLM", section 4: a query sees only keys at
   positions up to its own (later positions are masked out before the
   softmax), applied at an offset for a query chunk that ends at the
@@ -124,6 +129,42 @@ def write(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray, v_new: np.n
             kf[s] = k_new[t]
             vf[s] = v_new[t]
     return kp, vp
+
+
+def index_errors(slots, tables, context_lens, num_blocks: int, block_size: int) -> dict:
+    """What a debug check of the index data counts, by definition.
+
+    Each token is written once ("Build a Mini vLLM", section 4) and a table
+    names pool blocks ("nano-vLLM", "How it works"); the kernels skip or mask
+    whatever breaks this, so these counts name the caller's errors:
+    slots below 0, slots at or past ``num_blocks * block_size``, duplicate
+    slots (a slot named by k tokens adds k - 1), table entries outside
+    ``[0, num_blocks)`` among the ``ceil(ctx / block_size)`` blocks a sequence
+    needs (its context clamped to the table), and context lengths below 0 or
+    past the table's reach. ``slots`` or ``tables`` may be None.
+    """
+    n_slots = num_blocks * block_size
+    neg = past = dup = 0
+    seen = {}
+    for s in ([] if slots is None else [int(x) for x in np.asarray(slots).ravel()]):
+        if s < 0:
+            neg += 1
+        elif s >= n_slots:
+            past += 1
+        else:
+            seen[s] = seen.get(s, 0) + 1
+    dup = sum(c - 1 for c in seen.values())
+    bad = outside = 0
+    if tables is not None:
+        tables = np.asarray(tables)
+        for row, c in zip(tables, np.asarray(context_lens).ravel()):
+            c = int(c)
+            if c < 0 or c > len(row) * block_size:
+                outside += 1
+            need = -(-_clamp_ctx(c, len(row), block_size) // block_size)
+            bad += sum(1 for b in row[:need] if not 0 <= int(b) < num_blocks)
+    return {"negative_slots": neg, "slots_past_pool": past, "duplicate_slots": dup,
+            "invalid_table_entries": bad, "context_past_table": outside}
 
 
 # --------------------------------------------------------------------------

@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     PkvError,
     PreparedCall,
     PoolDesc,
+    VALIDATE_FIELDS,
     abi_version,
     block_bytes,
     decode,
@@ -22,6 +23,7 @@ from ._binding import (  # noqa: F401
     decode_step_noalloc,
     decode_partition,
     decode_workspace_bytes,
+    debug_enabled,
     load,
     plan_pool,
     pool_desc,
@@ -29,5 +31,6 @@ from ._binding import (  # noqa: F401
     prepare_decode_step,
     prefill,
     slot_mapping,
+    validate,
     write,
 )

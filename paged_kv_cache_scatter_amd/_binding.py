@@ -30,6 +30,7 @@ EXPORTS = ("pkv_slot_mapping", "pkv_write", "pkv_decode_partition",
            "pkv_decode_reduce", "pkv_decode_step", "pkv_decode_step_partials",
            "pkv_decode_step_noalloc",
            "pkv_decode_shared_workspace_bytes", "pkv_decode_shared", "pkv_prefill",
+           "pkv_validate_workspace_bytes", "pkv_validate",
            "pkv_block_bytes", "pkv_plan_pool", "pkv_status_string", "pkv_last_error",
            "pkv_abi_version")
 
@@ -95,6 +96,10 @@ def load(path: str | None = None):
     lib.pkv_prefill.argtypes = [_P, _P, _I, _I, _I, _I, _P, _P, ctypes.POINTER(PoolDesc), _P,
                                 _I, _P, _I, ctypes.c_float, _P, _P]
     lib.pkv_prefill.restype = ctypes.c_int
+    lib.pkv_validate_workspace_bytes.argtypes = [_I, _I]
+    lib.pkv_validate_workspace_bytes.restype = ctypes.c_size_t
+    lib.pkv_validate.argtypes = [_P, _I, _P, _I, _P, _I, _I, _I, _P, ctypes.c_size_t, _P, _P]
+    lib.pkv_validate.restype = ctypes.c_int
     lib.pkv_block_bytes.argtypes = [_I, _I, _I, _I, _I]
     lib.pkv_block_bytes.restype = ctypes.c_int64
     lib.pkv_plan_pool.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_double, ctypes.c_int64,
@@ -225,6 +230,10 @@ def write(k: torch.Tensor, v: torch.Tensor, slots: torch.Tensor, k_pool: torch.T
     T = slots.shape[0]
     _dev(k, "k", k_pool.dtype, (T, desc.num_kv_heads, desc.head_dim))
     _dev(v, "v", k_pool.dtype, (T, desc.num_kv_heads, desc.head_dim))
+    if debug_enabled():
+        _debug_check("write", validate(slots=slots, num_blocks=desc.num_blocks,
+                                       block_size=desc.block_size), ("slots_past_pool",
+                                                                     "duplicate_slots"))
     _check(load().pkv_write(_ptr(k), _ptr(v), _ptr(slots), T, _ptr(k_pool), _ptr(v_pool),
                             ctypes.byref(desc), _stream()))
 
@@ -261,6 +270,7 @@ def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     """
     fn, args, keep = _decode_call(q, k_pool, v_pool, block_tables, context_lens, scale,
                                   max_context_len, out, partition, workspace, phase)
+    _debug_tables("decode", k_pool, block_tables, context_lens)
     _check(getattr(load(), fn)(*args, _stream()))
     return keep[-1]
 
@@ -306,6 +316,7 @@ def prepare_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     launches the same decode on the current stream each time it is called."""
     fn, args, keep = _decode_call(q, k_pool, v_pool, block_tables, context_lens, scale,
                                   max_context_len, out, partition, workspace, "both")
+    _debug_tables("prepare_decode", k_pool, block_tables, context_lens)
     return PreparedCall(fn, args, q.device, keep, keep[-1])
 
 
@@ -358,6 +369,7 @@ def decode_shared(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     if workspace is not None:
         _dev(workspace, "workspace", torch.uint8)
         ws_bytes = workspace.numel()
+    _debug_tables("decode_shared", k_pool, block_tables, context_lens)
     _check(load().pkv_decode_shared(
         _ptr(q), S, Hq, _ptr(k_pool), _ptr(v_pool), ctypes.byref(desc), _ptr(block_tables), maxb,
         _ptr(context_lens), int(max_context_len), _ptr(group_start), _ptr(prefix_lens), G,
@@ -378,6 +390,7 @@ def decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
     ``decode(..., phase="reduce")`` with the same arguments) or "reduce"."""
     fn, args, keep = _step_call(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens,
                                 scale, max_context_len, out, partition, workspace, phase)
+    _debug_tables("decode_step", k_pool, block_tables, context_lens)
     _check(getattr(load(), fn)(*args, _stream()))
     return keep[-1]
 
@@ -430,6 +443,7 @@ def prepare_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tenso
     launches the same fused step on the current stream each time it is called."""
     fn, args, keep = _step_call(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens,
                                 scale, max_context_len, out, partition, workspace, "both")
+    _debug_tables("prepare_decode_step", k_pool, block_tables, context_lens)
     return PreparedCall(fn, args, q.device, keep, keep[-1])
 
 
@@ -455,6 +469,7 @@ def decode_step_noalloc(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tenso
           "block_tables must be [S, max_blocks_per_seq]")
     _dev(context_lens, "context_lens", torch.int32, (S,))
     _dev(out, "out", q.dtype, q.shape)
+    _debug_tables("decode_step_noalloc", k_pool, block_tables, context_lens)
     _check(load().pkv_decode_step_noalloc(
         _ptr(q), _ptr(k_new), _ptr(v_new), S, Hq, _ptr(k_pool), _ptr(v_pool), ctypes.byref(desc),
         _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), int(max_context_len),
@@ -480,6 +495,7 @@ def prefill(q: torch.Tensor, cu_q: torch.Tensor, k_pool: torch.Tensor, v_pool: t
     if out is None:
         out = torch.empty_like(q)
     _dev(out, "out", q.dtype, q.shape)
+    _debug_tables("prefill", k_pool, block_tables, context_lens)
     _check(load().pkv_prefill(_ptr(q), _ptr(cu_q), S, Hq, int(max_q_len), R, _ptr(k_pool),
                               _ptr(v_pool), ctypes.byref(desc), _ptr(block_tables), maxb,
                               _ptr(context_lens), int(max_context_len), float(scale), _ptr(out),
@@ -489,6 +505,72 @@ def prefill(q: torch.Tensor, cu_q: torch.Tensor, k_pool: torch.Tensor, v_pool: t
 
 def abi_version() -> int:
     return int(load().pkv_abi_version())
+
+
+# ---------------------------------------------------------------- index checks
+VALIDATE_FIELDS = ("negative_slots", "slots_past_pool", "duplicate_slots",
+                   "invalid_table_entries", "context_past_table")
+
+
+def validate(slots: torch.Tensor | None = None, block_tables: torch.Tensor | None = None,
+             context_lens: torch.Tensor | None = None, *, num_blocks: int, block_size: int,
+             workspace: torch.Tensor | None = None) -> dict:
+    """Counts of the index errors the kernels would silently skip or mask
+    (``pkv_validate``): slots < 0, slots past the pool, duplicate slots of one
+    write, table entries outside the pool among the blocks a sequence needs,
+    and context lengths outside the table's reach. Synchronises the current
+    stream to read the counts. ``workspace``: a zeroed int32 device tensor of
+    ``pkv_validate_workspace_bytes`` bytes (allocated here if omitted; left
+    zero by the call)."""
+    lib = load()
+    dev = next((t.device for t in (slots, block_tables) if t is not None), None)
+    _need(dev is not None, "validate needs slots or block_tables")
+    T, S, maxb = 0, 0, 0
+    if slots is not None:
+        _dev(slots, "slot_mapping", torch.int32)
+        _need(slots.dim() == 1, "slot_mapping must be 1-D")
+        T = slots.shape[0]
+    if block_tables is not None:
+        _dev(block_tables, "block_tables", torch.int32)
+        _need(block_tables.dim() == 2, "block_tables must be [S, max_blocks_per_seq]")
+        S, maxb = block_tables.shape
+        _need(context_lens is not None, "checking tables needs context_lens")
+        _dev(context_lens, "context_lens", torch.int32, (S,))
+    ws_bytes = 0
+    if T > 0:
+        need = int(lib.pkv_validate_workspace_bytes(int(num_blocks), int(block_size)))
+        if workspace is None:
+            workspace = torch.zeros((need + 3) // 4, dtype=torch.int32, device=dev)
+        _dev(workspace, "workspace", torch.int32)
+        ws_bytes = workspace.numel() * 4
+    report = torch.empty(len(VALIDATE_FIELDS), dtype=torch.int32, device=dev)
+    _check(lib.pkv_validate(_ptr(slots), T, _ptr(block_tables), maxb, _ptr(context_lens), S,
+                            int(num_blocks), int(block_size), _ptr(workspace), ws_bytes,
+                            _ptr(report), _stream()))
+    return dict(zip(VALIDATE_FIELDS, (int(x) for x in report.cpu())))
+
+
+def debug_enabled() -> bool:
+    """PKV_DEBUG set to anything but "" or "0": the plain binding functions
+    validate their index arguments (one extra synchronisation per call) and
+    raise PkvError on what the kernels would silently skip or mask. Prepared
+    calls are checked once, when prepared."""
+    return os.environ.get("PKV_DEBUG", "") not in ("", "0")
+
+
+def _debug_check(what: str, counts: dict, fatal: tuple):
+    bad = {k: counts[k] for k in fatal if counts[k]}
+    if bad:
+        raise PkvError(3, f"PKV_DEBUG: {what}: " +   # PKV_ERR_SHAPE
+                       ", ".join(f"{k} {n}" for k, n in bad.items()))
+
+
+def _debug_tables(what: str, k_pool: torch.Tensor, block_tables: torch.Tensor,
+                  context_lens: torch.Tensor):
+    if debug_enabled():
+        _debug_check(what, validate(block_tables=block_tables, context_lens=context_lens,
+                                    num_blocks=k_pool.shape[0], block_size=k_pool.shape[1]),
+                     ("invalid_table_entries", "context_past_table"))
 
 
 # ---------------------------------------------------------------- pool sizing

@@ -817,6 +817,64 @@ pkv_status pkv_prefill(const void* q, const int32_t* cu_q, int32_t num_seqs, int
                         reinterpret_cast<hipStream_t>(stream));
 }
 
+size_t pkv_validate_workspace_bytes(int32_t num_blocks, int32_t block_size) {
+  if (num_blocks < 1 || block_size < 1) return 0;
+  const int64_t slots = (int64_t)num_blocks * block_size;
+  return (size_t)((slots + 31) / 32) * 4;
+}
+
+pkv_status pkv_validate(const int32_t* slot_mapping, int32_t num_tokens,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        const int32_t* context_lens, int32_t num_seqs, int32_t num_blocks,
+                        int32_t block_size, void* workspace, size_t workspace_bytes,
+                        int32_t* report, void* stream) {
+  if (!report) {
+    set_error("report must not be NULL");
+    return PKV_ERR_NULL;
+  }
+  if (num_tokens < 0 || num_seqs < 0 || num_blocks < 1) {
+    set_error("bad sizes: num_tokens %d, num_seqs %d, num_blocks %d", num_tokens, num_seqs,
+              num_blocks);
+    return PKV_ERR_SHAPE;
+  }
+  if (!is_pow2(block_size) || block_size > 256) {
+    set_error("block_size %d must be a power of two in [1, 256]", block_size);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if ((int64_t)num_blocks * block_size > INT32_MAX) {
+    set_error("num_blocks * block_size exceeds int32 slots");
+    return PKV_ERR_UNSUPPORTED;
+  }
+  const bool slots = slot_mapping && num_tokens > 0;
+  const bool tables = block_tables && num_seqs > 0;
+  if (num_seqs > 0 && block_tables && (!context_lens || max_blocks_per_seq < 1)) {
+    set_error("checking tables needs context_lens and max_blocks_per_seq >= 1");
+    return context_lens ? PKV_ERR_SHAPE : PKV_ERR_NULL;
+  }
+  if (slots) {
+    const size_t need = pkv_validate_workspace_bytes(num_blocks, block_size);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 3)) {
+      set_error("checking slots needs a zeroed, 4-byte aligned workspace of %zu bytes "
+                "(got %zu)", need, workspace_bytes);
+      return PKV_ERR_WORKSPACE;
+    }
+  }
+  ValidateArgs a;
+  a.slots = slot_mapping;
+  a.tables = block_tables;
+  a.ctx_lens = context_lens;
+  a.bits = static_cast<uint32_t*>(workspace);
+  a.report = report;
+  a.pool_slots = (int64_t)num_blocks * block_size;
+  a.num_tokens = slots ? num_tokens : 0;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_seqs = tables ? num_seqs : 0;
+  a.block_shift = ilog2(block_size);
+  a.num_blocks = num_blocks;
+  launch_validate(a, reinterpret_cast<hipStream_t>(stream));
+  return launch_status("validate kernels");
+}
+
 int64_t pkv_block_bytes(int32_t num_layers, int32_t block_size, int32_t num_kv_heads,
                         int32_t head_dim, int32_t itemsize) {
   if (num_layers < 1 || block_size < 1 || num_kv_heads < 1 || head_dim < 1 || itemsize < 1)

@@ -42,6 +42,18 @@ struct WriteArgs {
 };
 void launch_write(const WriteArgs& a, bool vec16, int elem_bytes, hipStream_t st);
 
+constexpr int kValidateFields = 5;
+struct ValidateArgs {
+  const int32_t* slots;
+  const int32_t* tables;
+  const int32_t* ctx_lens;
+  uint32_t* bits;        // one bit per pool slot, zero on entry and on exit
+  int32_t* report;       // kValidateFields counters
+  int64_t pool_slots;
+  int32_t num_tokens, max_blocks, num_seqs, block_shift, num_blocks;
+};
+void launch_validate(const ValidateArgs& a, hipStream_t st);
+
 // Shared-prefix decode: groups of consecutive sequences whose block tables
 // begin with the same blocks. Group i holds sequences group_start[i] ..
 // group_start[i+1]-1 and shares its first prefix_lens[i] tokens (rounded down

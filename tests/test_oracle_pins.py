@@ -436,3 +436,38 @@ def test_prefill_rows_before_position_zero_are_zero():
                          wl.scale, "f32")
     assert not out[:3].any()
     assert np.isfinite(out).all() and out[3:].any()
+
+
+def test_index_errors_worked_example():
+    # pool of 64 blocks x 16 slots = 1024 slots, counted by hand:
+    # slots: -1 (negative), 3 three times (two duplicates), 1024 and 5000 (past
+    # the pool), 100 and 1023 (fine)
+    slots = [-1, 3, 3, 3, 1024, 100, 5000, 1023]
+    # tables: row 0 needs 3 blocks for ctx 40 and its third entry (70) is past
+    # the pool; row 1 needs 2 blocks for ctx 20, its second entry is negative;
+    # row 2's ctx 49 is past its 3-block reach (48), its entries are fine;
+    # row 3's ctx -2 is negative and needs no block; row 4 needs 1 block for
+    # ctx 1 and the bad entry after it is never needed
+    tables = [[0, 1, 70], [2, -4, 9], [5, 6, 7], [-1, -1, -1], [8, 99, 99]]
+    ctx = [40, 20, 49, -2, 1]
+    assert oracle.index_errors(slots, tables, ctx, 64, 16) == {
+        "negative_slots": 1, "slots_past_pool": 2, "duplicate_slots": 2,
+        "invalid_table_entries": 2, "context_past_table": 2}
+    assert oracle.index_errors(None, tables, ctx, 64, 16)["duplicate_slots"] == 0
+    assert oracle.index_errors(slots, None, None, 64, 16)["invalid_table_entries"] == 0
+
+
+def test_index_errors_on_shared_prefix_tables():
+    # "nano-vLLM" "How it works": two sequences whose tables [1, 2, 5] and
+    # [1, 2, 6] share a 32-token prompt (block 16). Writing the prompt once and
+    # each sequence's own tokens is clean; writing the prompt for both
+    # sequences sends 32 tokens to slots already named: 32 duplicates.
+    tables = np.array([[1, 2, 5], [1, 2, 6]], np.int32)
+    own = oracle.slot_mapping(tables, np.array([32, 32]), np.array([0, 8, 16]), 16, 8)
+    prompt = oracle.slot_mapping(tables[:1], np.array([0]), np.array([0, 32]), 16, 8)
+    clean = np.concatenate([prompt, own])
+    assert oracle.index_errors(clean, tables, [40, 40], 8, 16) == {
+        "negative_slots": 0, "slots_past_pool": 0, "duplicate_slots": 0,
+        "invalid_table_entries": 0, "context_past_table": 0}
+    twice = oracle.slot_mapping(tables, np.array([0, 0]), np.array([0, 40, 80]), 16, 8)
+    assert oracle.index_errors(twice, tables, [40, 40], 8, 16)["duplicate_slots"] == 32
