@@ -47,7 +47,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import paged_kv_cache_scatter_amd as pkv  # noqa: E402
-from workloads import CONFIGS, make_shared, make_workload  # noqa: E402
+from workloads import CONFIGS, make_shared, make_tp_shard, make_workload  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 DEV = torch.device("cuda:0")
@@ -312,10 +312,11 @@ def time_prefill(step: Step, calls: int = 10, warmup: int = 10):
                          "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}}
 
 
-def time_decode_rotating(cfg: int, calls_per_set: int = 10):
+def time_decode_rotating(cfg: int, calls_per_set: int = 10, wl=None):
     """Decode-only timing (partials + merge) cycling over disjoint block sets of
-    one pool, so consecutive calls do not hit the Infinity Cache."""
-    wl = make_workload(cfg)
+    one pool, so consecutive calls do not hit the Infinity Cache. ``wl``
+    replaces configuration ``cfg``'s workload (e.g. one rank's shard of it)."""
+    wl = make_workload(cfg) if wl is None else wl
     print(f"[bench] rotating decode timing, {wl.name}", file=sys.stderr, flush=True)
     need = int(sum(-(-int(c) // wl.block_size) for c in wl.context_lens))
     sets = max(1, min(24, (wl.num_blocks - 1) // need))
@@ -395,7 +396,7 @@ def time_decode_rotating(cfg: int, calls_per_set: int = 10):
         graph.replay()
         torch.cuda.synchronize()
         if not torch.equal(out, eager_out):
-            raise SystemExit(f"config {cfg}: graph replay differs from the eager calls")
+            raise SystemExit(f"{wl.name}: graph replay differs from the eager calls")
     reps = 5
     # warm: the same block set back to back (its K/V stay in the Infinity Cache
     # when they fit: cache-assisted)
@@ -413,7 +414,7 @@ def time_decode_rotating(cfg: int, calls_per_set: int = 10):
     torch.cuda.synchronize()
     ms_graph = e0.elapsed_time(e1) / (reps * n)
     if not torch.equal(out, eager_out):
-        raise SystemExit(f"config {cfg}: graph replay differs from the eager calls")
+        raise SystemExit(f"{wl.name}: graph replay differs from the eager calls")
     kvb = wl.kv_bytes_per_call()
     return {"name": wl.name, "workload": workload_label(wl), "partition": part,
             "rotating_sets": sets,
@@ -1083,6 +1084,9 @@ def main():
                 continue
             r = time_decode_rotating(cfg)
             extra[r.pop("name")] = r
+        # one rank's share of the 70B layer with its KV heads over 8 GPUs
+        r = time_decode_rotating(5, wl=make_tp_shard(5, 8))
+        extra[r.pop("name")] = r
         res["other_workloads_decode_only"] = extra
     res.update(cpu_legs)
     print(json.dumps(res), flush=True)

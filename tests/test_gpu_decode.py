@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import paged_kv_cache_scatter_amd as pkv
-from workloads import make_custom, make_workload
+from workloads import make_custom, make_tp_shard, make_workload
 
 from _gpu_util import PoolCase, bits, check_close, note, out_f64, to_dev, to_host
 
@@ -43,6 +43,17 @@ def test_decode_full_size_every_sequence(cfg):
     got = out_f64(pc.decode(), pc.wl.dtype)
     ref = pc.ref_decode()
     err = check_close(got, ref, pc.wl.dtype, pc.wl.name)
+    note(f"{pc.wl.name}: all {pc.wl.num_seqs} sequences, max error {err:.3e}")
+
+
+def test_tp8_shard_of_the_70b_layer_every_sequence():
+    """One rank's share of the 70B layer with its 8 KV heads split over 8 GPUs
+    (1 KV head, 8 query heads, head_dim 128, the layer's lengths and tables):
+    only 64 (sequence, KV head) units, so the planner splits every long
+    context. Every output of every sequence against the oracle."""
+    pc = PoolCase(make_tp_shard(5, 8))
+    got = out_f64(pc.decode(), pc.wl.dtype)
+    err = check_close(got, pc.ref_decode(), pc.wl.dtype, pc.wl.name)
     note(f"{pc.wl.name}: all {pc.wl.num_seqs} sequences, max error {err:.3e}")
 
 

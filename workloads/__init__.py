@@ -7,5 +7,5 @@ oracle (``oracle/``) and the HIP path consume what it returns.
 """
 
 from .gen import (CONFIGS, Workload, kv_bytes, make_custom, make_layers,  # noqa: F401
-                  make_shared, make_workload, poison_pool)
+                  make_shared, make_tp_shard, make_workload, poison_pool)
 from .engine import TokenRows, engine_requests  # noqa: F401

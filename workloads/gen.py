@@ -291,6 +291,30 @@ def make_workload(cfg_id: int, num_seqs: int | None = None, seed: int | None = N
                   paired_write=spec.paired_write, prefill_chunk=spec.prefill_chunk)
 
 
+def make_tp_shard(cfg_id: int = 5, tp: int = 8) -> Workload:
+    """One rank's share of configuration ``cfg_id`` when its KV heads are split
+    over ``tp`` GPUs: the same context lengths and block tables (one table
+    serves every rank), ``num_kv_heads / tp`` KV heads and their query heads,
+    fresh N(0,1) values at that shape. For the 70B layer (8 KV heads) and
+    tp = 8 this is 1 KV head and 8 query heads, head_dim 128."""
+    spec = CONFIGS[cfg_id]
+    assert spec.num_kv_heads % tp == 0, "tp must divide the KV heads"
+    g = torch.Generator().manual_seed(1000 + cfg_id)
+    ctx = _draw_ctx(spec, spec.num_seqs, g)
+    first_free = 1 + spec.prefix_blocks
+    order = (torch.randperm(spec.num_blocks - first_free, generator=g).numpy()
+             + first_free).astype(np.int32)
+    prefix_ids = list(range(1, 1 + spec.prefix_blocks))
+    tables = _fill_tables(ctx, spec.block_size, spec.max_blocks_per_seq, order, prefix_ids)
+    hkv = spec.num_kv_heads // tp
+    hq = spec.num_q_heads // tp
+    # cfg_id names the configuration whose lengths and tables the shard keeps
+    return _build(f"{spec.name}-tp{tp}-shard", cfg_id, spec.dtype, hq, hkv, spec.head_dim,
+                  spec.block_size, spec.num_blocks, spec.max_blocks_per_seq,
+                  1.0 / math.sqrt(spec.head_dim), ctx, tables,
+                  spec.prefix_blocks * spec.block_size, g, paired_write=spec.paired_write)
+
+
 def make_custom(tables, context_lens, *, dtype=F32, num_q_heads=2, num_kv_heads=1,
                 head_dim=16, block_size=16, num_blocks=None, prefix_tokens=0,
                 scale=None, seed=0, name="custom") -> Workload:
