@@ -654,8 +654,8 @@ def _oracle_worker(args):
 
 
 def host_cores() -> int:
-    """CPU threads this process may use: its affinity set, at most 16 (a
-    one-GPU machine's share of its host)."""
+    """CPU threads this process may use: its affinity set, at most 16 (the
+    share of a multi-GPU host's cores that one GPU's process gets)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
