@@ -136,9 +136,9 @@ pkv_status pkv_write(const void* k, const void* v, const int32_t* slot_mapping,
  * see pkv_decode_partition). With at most 1024 sequences, a power-of-two
  * partition and pieces of at least 128 KiB of K and V (smaller ones finish
  * before a schedule pays) the cut is finer: each context gets full pieces of
- * `partition` tokens; a rest shorter than a quarter of it joins the last
- * full piece, a longer one becomes one or two near-equal tail pieces of at
- * most about half a partition; the launch runs all full pieces first, then
+ * `partition` tokens; a rest shorter than half of it joins the last full
+ * piece, a longer one becomes one tail piece of its own (shorter than a
+ * partition); the launch runs all full pieces first, then
  * the tail pieces, longer ones first (near-equal pieces keep every workgroup
  * stream of the GPU equally loaded and the last pieces short). Each piece of
  * a sequence with more than one yields a partial (running max m in log2

@@ -86,11 +86,11 @@ def test_decode_argument_errors(lib):
 
 def test_workspace_bytes(lib):
     d = _desc(nb=32769, bs=16, hkv=8, hd=128)
-    # 64 sequences x 64 heads x 10 partial slots: a context of up to 8192
-    # tokens has at most 8 pieces of 1024 tokens and 2 tail pieces of at most
-    # 512 (slots: 8192 / 1024 + ceil(1023 / 512)); the fixed merge counter
+    # 64 sequences x 64 heads x 9 partial slots: a context of up to 8192
+    # tokens has at most 8 pieces of 1024 tokens and 1 tail piece of less than
+    # 1024 (slots: 8192 / 1024 + ceil(1023 / 1024)); the fixed merge counter
     # area (65536 int32), then (m, l), then o[128], each part 256-byte aligned
-    rows = 64 * 64 * 10
+    rows = 64 * 64 * 9
     assert lib.pkv_decode_workspace_bytes(64, 64, 8192, 1024, ctypes.byref(d)) == \
         COUNTER_AREA + rows * 2 * 4 + rows * 128 * 4
     assert lib.pkv_decode_workspace_bytes(64, 64, 1024, 1024, ctypes.byref(d)) == 0
@@ -210,13 +210,15 @@ def test_piece_schedule_needs_large_pieces(lib):
     carries at least 128 KiB of K and V."""
     d = _desc(nb=32769, bs=16, hkv=8, hd=128)    # bf16 rows: 512 bytes of K+V per token
 
-    def slots(part, max_ctx=4000):
+    # (a multiple of the partition, so that the schedule's one slot for a
+    # tail piece shows against the plain grid's ceil(max_ctx / partition))
+    def slots(part, max_ctx=4096):
         rows = 64 * 64
         b = lib.pkv_decode_workspace_bytes(64, 64, max_ctx, part, ctypes.byref(d))
         return (b - COUNTER_AREA) // (rows * (2 + 128) * 4)
-    assert slots(128) == -(-4000 // 128)           # 64 KiB pieces: plain grid
-    assert slots(256) == 4000 // 256 + 2           # 128 KiB pieces: schedule, up to two tails
-    assert slots(1024) == 4000 // 1024 + 2         # up to two tails of 512
+    assert slots(128) == 4096 // 128               # 64 KiB pieces: plain grid
+    assert slots(256) == 4096 // 256 + 1           # 128 KiB pieces: schedule, one tail slot
+    assert slots(1024) == 4096 // 1024 + 1
 
 
 def test_partition_validity_does_not_depend_on_pairing(lib):
