@@ -859,15 +859,27 @@ def phase_trace(cfg: int):
             "alive": [int(((start <= b) & (end > b)).sum()) for b in bins]}
 
 
-def traffic_from_counters(kernel_src: str):
+# Sources that decide what the dominant launch reads and writes: the kernel,
+# the planner that sizes its pieces and partials, and their shared header.
+COUNTED_SOURCES = ("pkv_decode.hip", "pkv_api.hip", "pkv_internal.h")
+
+
+def counted_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for name in COUNTED_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_scatter_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_from_counters():
     """HBM bytes per launch measured by rocprofv3 counters, if they were taken on
-    the current kernel source; else None."""
+    the current kernel and planner sources; else None."""
     if not os.path.exists(COUNTERS):
         return None
     with open(COUNTERS) as f:
         c = json.load(f)
-    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
-    if c.get("kernel_source_sha256") != sha:
+    if c.get("sources_sha256") != counted_sources_sha256():
         return None
     return c.get("hbm_bytes_per_launch")
 
@@ -915,9 +927,9 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, cop
     cw, _ = mean_of(_counter_rows(copy_write_dir, "WRITE_SIZE"), "copy")
     sf = copy_bytes / (cf * 1024.0)
     sw = copy_bytes / (cw * 1024.0)
-    src = os.path.join(ROOT, "paged_kv_cache_scatter_amd", "csrc", "pkv_decode.hip")
     out = {"kernel": kernel_key,
-           "kernel_source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+           "sources": list(COUNTED_SOURCES),
+           "sources_sha256": counted_sources_sha256(),
            "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
            "dispatches": [nf, nw],
            "copy_bytes": copy_bytes, "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1),
@@ -1021,8 +1033,7 @@ def main():
     # duration is the step time between the events around the timed loop
     ms_kernel = ms_step
     achieved = kvb / (ms_kernel * 1e-3) / 1e9
-    src = os.path.join(ROOT, "paged_kv_cache_scatter_amd", "csrc", "pkv_decode.hip")
-    traffic = traffic_from_counters(src)
+    traffic = traffic_from_counters()
     res = {
         "metric": "paged decode attention: achieved KV-read GB/s and % HBM peak; seq-steps/s",
         "value": round(gbs, 1),
