@@ -269,3 +269,23 @@ def test_shared_prefix_planner_falls_back_below_the_saved_bytes_bound(lib, monke
     assert shared() > plain
     monkeypatch.setenv("PKV_SHARED_MIN_SAVED_BYTES", str(22093825))
     assert shared() == plain
+
+
+def test_missing_library_fails_loudly():
+    """Without libpkv.so the binding raises on load and on any call; there is
+    no CPU fallback. Run in a fresh interpreter (the handle is cached)."""
+    import subprocess
+    import sys
+    code = (
+        "import paged_kv_cache_scatter_amd._binding as b\n"
+        "b.LIB_PATH = '/nonexistent/libpkv.so'\n"
+        "for f in (b.load, lambda: b.block_bytes(1, 16, 8, 128, 2)):\n"
+        "    try:\n"
+        "        f()\n"
+        "        print('no error')\n"
+        "    except RuntimeError as e:\n"
+        "        print('raised', 'not built' in str(e))\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=root,
+                       timeout=300)
+    assert r.stdout.split("\n")[:2] == ["raised True", "raised True"], r.stdout + r.stderr
