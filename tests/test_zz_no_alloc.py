@@ -62,3 +62,46 @@ def test_noalloc_step_matches_workspace_step(cfg, sizes):
         err = check_close(oracle.storage_to_f64(o_na, wl.dtype), ref, wl.dtype, wl.name)
         note(f"{wl.name}: {S} sequences bit-identical to the workspace form, "
              f"max error {err:.3e}")
+
+
+def test_noalloc_step_replays_from_a_captured_graph():
+    """The callers the no-alloc entry point is for include code under HIP graph
+    capture: after one eager call (which locates the scratch array on this
+    device), the step is captured and replayed, with eager calls on other
+    inputs in between, and every replay reproduces the eager bits."""
+    wl = make_workload(5, num_seqs=16)
+    rows = _rows(wl)
+    kn, vn = to_dev(wl.k_rows[rows]), to_dev(wl.v_rows[rows])
+    pc = PoolCase(wl, exclude_last=True)
+
+    def step(out):
+        return pkv.decode_step_noalloc(pc.q, kn, vn, pc.k_pool, pc.v_pool, pc.tables, pc.ctx,
+                                       wl.scale, pc.max_ctx, out=out)
+
+    eager = torch.full_like(pc.q, float("nan"))
+    step(eager)
+    torch.cuda.synchronize()
+    other = make_workload(5, num_seqs=5, seed=77)     # a different call sharing the scratch
+    po = PoolCase(other, exclude_last=True)
+    orows = _rows(other)
+    okn, ovn = to_dev(other.k_rows[orows]), to_dev(other.v_rows[orows])
+    out_g = torch.full_like(pc.q, float("nan"))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        note(f"{wl.name}: capturing pkv_decode_step_noalloc")
+        with torch.cuda.graph(g):
+            step(out_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for r in range(3):
+        out_g.fill_(float("nan"))
+        note(f"{wl.name}: replay {r}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(to_host(out_g)), bits(to_host(eager))), f"replay {r}"
+        o2 = torch.empty_like(po.q)
+        pkv.decode_step_noalloc(po.q, okn, ovn, po.k_pool, po.v_pool, po.tables, po.ctx,
+                                other.scale, po.max_ctx, out=o2)
+        torch.cuda.synchronize()
