@@ -246,3 +246,30 @@ def test_step_write_then_decode_llama1b_192_sequences():
     full.tabs, full.first, full.cu, full.rows = wl.bulk_segments()
     full._ref_pools = None
     check_close(got, full.ref_decode(), "bf16", wl.name)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("hd,hq,hkv,partition", [(64, 9, 3, 0), (64, 32, 8, 0), (128, 64, 8, 0),
+                                                 (128, 64, 8, 64)])
+def test_zero_queries_average_v(dtype, hd, hq, hkv, partition):
+    """q = 0 makes every score 0, so the softmax weights are equal and each
+    head's output is the plain mean of its KV head's V rows over the context:
+    a closed form computed here from the written rows, not by the oracle.
+    Automatic and forced (many-split) partitions."""
+    lens = [1, 17, 200, 513]
+    rng = np.random.default_rng(hd + hq)
+    need = [-(-L // 16) for L in lens]
+    perm = (rng.permutation(sum(need) + 5) + 1).tolist()
+    tabs, k = [], 0
+    for n in need:
+        tabs.append(perm[k:k + n])
+        k += n
+    wl = make_custom(tabs, lens, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv, head_dim=hd,
+                     block_size=16, num_blocks=sum(need) + 6, seed=hd)
+    pc = PoolCase(wl)
+    got = out_f64(pc.decode(partition=partition, q=torch.zeros_like(pc.q)), dtype)
+    v = oracle.storage_to_f64(wl.v_rows, dtype)          # [rows, Hkv, hd]
+    heads = np.arange(hq) // (hq // hkv)
+    want = np.stack([v[wl.seq_rows[s]].mean(axis=0)[heads] for s in range(len(lens))])
+    err = check_close(got, want, dtype, f"zero queries hd={hd} partition={partition}")
+    note(f"zero queries, {dtype} hd={hd}: max error {err:.2e} against the mean of V")

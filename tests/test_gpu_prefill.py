@@ -238,3 +238,28 @@ def test_prefill_llama70b_layer_chunks():
                                  wl.scale, "bf16")
         check_close(got[r:r + 1], ref, "bf16", f"row {r} (sequence {s}, position {a})")
     note(f"checked {len(whole)} whole chunks and {len(rows) + len(others)} more rows")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("hd", [64, 128])
+def test_prefill_zero_queries_average_the_visible_v(dtype, hd):
+    """q = 0 gives every visible key the same weight: row i of a chunk (its
+    position a = ctx - q_len + i) is the mean of V over positions 0 .. a, a
+    closed form of the causal mask computed from the written rows (rows before
+    position 0 are zero). Matrix-core path, several query and key tiles."""
+    lens = [150, 70, 33, 300]
+    qlens = [150, 20, 40, 130]
+    rep = 4
+    pc, cu, q_rows = _case(lens, qlens, dtype, hd, rep, seed=hd)
+    got = out_f64(_run(pc, np.zeros_like(q_rows), cu, max(qlens)), dtype)
+    wl = pc.wl
+    v = oracle.storage_to_f64(wl.v_rows, dtype)
+    heads = np.arange(wl.num_q_heads) // rep
+    want = np.zeros_like(got)
+    for s, (L, n) in enumerate(zip(lens, qlens)):
+        for i in range(n):
+            a = L - n + i
+            if a >= 0:
+                want[cu[s] + i] = v[wl.seq_rows[s][:a + 1]].mean(axis=0)[heads]
+    err = check_close(got, want, dtype, f"prefill zero queries hd={hd}")
+    note(f"prefill zero queries, {dtype} hd={hd}: max error {err:.2e} against the mean of V")
