@@ -161,7 +161,9 @@ pkv_status pkv_write(const void* k, const void* v, const int32_t* slot_mapping,
  * A needed table entry outside [0, num_blocks) removes that block's tokens
  * from the softmax (no out-of-bounds read). Slots of a block past the
  * sequence's length may hold anything (NaN included): they are masked by
- * selection, never multiplied in ([NV] "Correctness").
+ * selection, never multiplied in ([NV] "Correctness"). Non-finite values in q
+ * or in the rows a sequence owns are not handled: the affected output rows
+ * are unspecified (no access leaves its bounds).
  * q, out, k_pool, v_pool must be 16-byte aligned.
  * Compiled set: head_dim in {16, 32, 64, 128, 256}; num_q_heads / num_kv_heads
  * in 1..8; block_size a power of two <= 256.
