@@ -28,7 +28,8 @@ launches after a 512 MiB cache-evicting write ("cold", percentiles), the
 decode-only configs the same block set back to back ("warm", cache-assisted),
 and the step the percentiles of its launches timed one by one. The workload's
 chunked-prefill variant (pkv_prefill on the same pools) is timed too and
-reported against the dense bf16 matrix-core peak.
+reported against the dense bf16 matrix-core peak, and so is the bulk write that
+stores such a chunk for every sequence (pkv_write, against HBM).
 """
 
 from __future__ import annotations
@@ -52,6 +53,7 @@ from workloads import CONFIGS, make_shared, make_tp_shard, make_workload  # noqa
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 DEV = torch.device("cuda:0")
 COUNTERS = os.path.join(ROOT, "profiles", "decode_partials_counters.json")
+WRITE_COUNTERS = os.path.join(ROOT, "profiles", "write_bulk_counters.json")
 
 
 def to_dev(a: np.ndarray) -> torch.Tensor:
@@ -310,6 +312,73 @@ def time_prefill(step: Step, calls: int = 10, warmup: int = 10):
             "roofline": {"bound": "mfma", "kernel": "prefill_mfma_kernel",
                          "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}}
+
+
+def time_bulk_write(wl, calls_per_set: int = 10, sets: int = 4):
+    """A bulk KV write at the workload's shape: every sequence stores a
+    ``prefill_chunk``-token chunk (``num_seqs * prefill_chunk`` token rows of K
+    and V) into blocks of its own, as before a chunked prefill. Calls cycle
+    over ``sets`` disjoint sets of source rows and destination blocks, so
+    neither side is served from the Infinity Cache of the previous call. Timed
+    twice: the write alone (slots computed once per set) and the slot mapping
+    followed by the write. Pools are the workload's shape, values random."""
+    n, S = wl.prefill_chunk, wl.num_seqs
+    T, bs = S * n, wl.block_size
+    assert n % bs == 0
+    per_seq = n // bs
+    need = S * per_seq
+    sets = max(1, min(sets, (wl.num_blocks - 1) // need))
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    k_pool = torch.zeros(wl.pool_shape, dtype=dt, device=DEV)
+    v_pool = torch.zeros_like(k_pool)
+    g = torch.Generator(device=DEV).manual_seed(11)
+    rng = np.random.default_rng(11)
+    perm = rng.permutation(wl.num_blocks - 1) + 1
+    cu = torch.arange(0, T + 1, n, dtype=torch.int32, device=DEV)
+    first = torch.zeros(S, dtype=torch.int32, device=DEV)
+    src, tabs, slots = [], [], []
+    for r in range(sets):
+        shape = (T, wl.num_kv_heads, wl.head_dim)
+        src.append((torch.randn(shape, generator=g, device=DEV).to(dt),
+                    torch.randn(shape, generator=g, device=DEV).to(dt)))
+        t = to_dev(perm[r * need:(r + 1) * need].reshape(S, per_seq).astype(np.int32))
+        tabs.append(t)
+        slots.append(pkv.slot_mapping(t, first, cu, T, bs, wl.num_blocks))
+    sl_buf = torch.empty(T, dtype=torch.int32, device=DEV)
+
+    turn = [0]
+
+    def run_write():
+        r = turn[0] % sets
+        turn[0] += 1
+        pkv.write(src[r][0], src[r][1], slots[r], k_pool, v_pool)
+
+    def run_both():
+        r = turn[0] % sets
+        turn[0] += 1
+        pkv.slot_mapping(tabs[r], first, cu, T, bs, wl.num_blocks, out=sl_buf)
+        pkv.write(src[r][0], src[r][1], sl_buf, k_pool, v_pool)
+
+    calls = calls_per_set * sets
+    out = {}
+    for name, fn in (("write", run_write), ("slot_mapping_and_write", run_both)):
+        warm_up(fn, 2 * sets)
+        out[name] = timed_loop(fn, calls)
+    isz = k_pool.element_size()
+    row = wl.num_kv_heads * wl.head_dim * isz
+    # K and V rows are each read once from the new-token buffers and written
+    # once into the pool; the write reads one 4-byte slot per token
+    nbytes = 4 * T * row + 4 * T
+    gbs = nbytes / (out["write"] * 1e-3) / 1e9
+    return {"workload": f"{workload_label(wl)}; bulk write of a {n}-token chunk per sequence "
+                        f"({T} token rows of K and V, {sets} rotating sets)",
+            "calls": calls, "ms_per_call": round(out["write"], 4),
+            "ms_per_call_with_slot_mapping": round(out["slot_mapping_and_write"], 4),
+            "bytes_per_call": nbytes,
+            "roofline": {"bound": "hbm", "kernel": "write_kernel", "achieved": round(gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": traffic_from_counters("write")}}
 
 
 def time_decode_rotating(cfg: int, calls_per_set: int = 10, wl=None):
@@ -859,27 +928,33 @@ def phase_trace(cfg: int):
             "alive": [int(((start <= b) & (end > b)).sum()) for b in bins]}
 
 
-# Sources that decide what the dominant launch reads and writes: the kernel,
-# the planner that sizes its pieces and partials, and their shared header.
-COUNTED_SOURCES = ("pkv_decode.hip", "pkv_api.hip", "pkv_internal.h")
+# Counter files under profiles/: the kernel they measure, and the sources
+# that decide what its launches read and write (the kernel, the planner or
+# launcher that sizes them, and their shared header).
+COUNTED = {
+    "decode": ("decode_partials_kernel<unsigned short, 128, 8, 0>", COUNTERS,
+               ("pkv_decode.hip", "pkv_api.hip", "pkv_internal.h")),
+    "write": ("write_kernel", WRITE_COUNTERS, ("pkv_write.hip", "pkv_api.hip", "pkv_internal.h")),
+}
 
 
-def counted_sources_sha256() -> str:
+def counted_sources_sha256(which: str = "decode") -> str:
     h = hashlib.sha256()
-    for name in COUNTED_SOURCES:
+    for name in COUNTED[which][2]:
         with open(os.path.join(ROOT, "paged_kv_cache_scatter_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def traffic_from_counters():
+def traffic_from_counters(which: str = "decode"):
     """HBM bytes per launch measured by rocprofv3 counters, if they were taken on
     the current kernel and planner sources; else None."""
-    if not os.path.exists(COUNTERS):
+    path = COUNTED[which][1]
+    if not os.path.exists(path):
         return None
-    with open(COUNTERS) as f:
+    with open(path) as f:
         c = json.load(f)
-    if c.get("sources_sha256") != counted_sources_sha256():
+    if c.get("sources_sha256") != counted_sources_sha256(which):
         return None
     return c.get("hbm_bytes_per_launch")
 
@@ -912,10 +987,12 @@ def _counter_rows(run_dir: str, counter: str):
 
 
 def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes,
-                       kernel_key="decode_partials_kernel<unsigned short, 128, 8, 0>"):
-    """HBM bytes per launch of the dominant kernel from four rocprofv3 --pmc runs
-    (FETCH_SIZE and WRITE_SIZE in KiB per dispatch, of the kernel and of a plain
-    copy of copy_bytes), each counter scaled by what it reads for the copy."""
+                       which: str = "decode"):
+    """HBM bytes per launch of a kernel (``which`` names it in COUNTED) from four
+    rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE in KiB per dispatch, of the
+    kernel and of a plain copy of copy_bytes), each counter scaled by what it
+    reads for the copy."""
+    kernel_key, out_path, sources = COUNTED[which]
     def mean_of(rows, key):
         v = [x for k, x in rows if key in k]
         if not v:
@@ -928,14 +1005,14 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, cop
     sf = copy_bytes / (cf * 1024.0)
     sw = copy_bytes / (cw * 1024.0)
     out = {"kernel": kernel_key,
-           "sources": list(COUNTED_SOURCES),
-           "sources_sha256": counted_sources_sha256(),
+           "sources": list(sources),
+           "sources_sha256": counted_sources_sha256(which),
            "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
            "dispatches": [nf, nw],
            "copy_bytes": copy_bytes, "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1),
            "fetch_scale": round(sf, 4), "write_scale": round(sw, 4),
            "hbm_bytes_per_launch": int(round(fk * 1024 * sf + wk * 1024 * sw))}
-    with open(COUNTERS, "w") as f:
+    with open(out_path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
 
@@ -968,6 +1045,10 @@ def main():
     ap.add_argument("--phase-trace", nargs="+", type=int, metavar="CFG",
                     help="only per-workgroup phase timings of one decode launch of these "
                          "configs, from the traced build (libpkv_trace.so)")
+    ap.add_argument("--counters-of", default="decode", choices=sorted(COUNTED),
+                    help="the kernel --summarize-counters measures")
+    ap.add_argument("--bulk-write-only", action="store_true",
+                    help="only the bulk-write leg (for kernel-trace and counter runs)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the chunked-prefill leg, two calls after one warm-up (for "
                          "counter runs)")
@@ -984,6 +1065,11 @@ def main():
         step = Step(make_workload(args.config), args.partition)
         print(json.dumps({"prefill": time_prefill(step, calls=2, warmup=1)}), flush=True)
         return
+    if args.bulk_write_only:
+        pkv.load()
+        print(json.dumps({"bulk_write": time_bulk_write(make_workload(args.config))}),
+              flush=True)
+        return
     if args.layer_graph:
         pkv.load()
         for cfg in args.layer_graph:
@@ -998,7 +1084,8 @@ def main():
             print(json.dumps({"shared_prefix_decode": time_shared(name)}), flush=True)
         return
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters, copy_bytes=512 << 20)
+        summarize_counters(*args.summarize_counters, copy_bytes=512 << 20,
+                           which=args.counters_of)
         return
     if args.copy_calibration:
         copy_calibration()
@@ -1076,6 +1163,8 @@ def main():
     if not args.no_extra and wl.prefill_chunk and wl.dtype == "bf16":
         print("[bench] chunked prefill", file=sys.stderr, flush=True)
         res["prefill"] = time_prefill(step)
+        print("[bench] bulk write of a prefill chunk per sequence", file=sys.stderr, flush=True)
+        res["bulk_write"] = time_bulk_write(wl)
     if not args.no_extra:
         del step
         torch.cuda.empty_cache()
