@@ -106,8 +106,13 @@ class Step:
         self.tables = to_dev(wl.block_tables)
         self.ctx = to_dev(wl.context_lens)
         self.max_ctx = int(wl.context_lens.max())
-        self.partition = partition or pkv.decode_partition(wl.num_seqs, self.max_ctx,
-                                                           self.k_pool)
+        # partition 0 leaves the cut to the library; auto_partition is the
+        # split size it would take (and the least stream-K range)
+        self.partition = partition
+        self.auto_partition = partition or pkv.decode_partition(wl.num_seqs, self.max_ctx,
+                                                                self.k_pool)
+        self.schedule = pkv.decode_schedule(wl.num_seqs, wl.num_q_heads, self.max_ctx,
+                                            self.k_pool, partition)
         nws = pkv.decode_workspace_bytes(wl.num_seqs, wl.num_q_heads, self.max_ctx,
                                          self.k_pool, self.partition)
         self.ws = torch.zeros(max(nws, 16), dtype=torch.uint8, device=DEV)
@@ -251,7 +256,7 @@ def time_probes(step: Step, calls: int = 20, stream_bytes: int = 2 << 30):
                                step.tables.data_ptr(), wl.block_tables.shape[1],
                                step.ctx.data_ptr(), wl.num_seqs, step.max_ctx,
                                wl.num_kv_heads, row_bytes, wl.block_size, wl.num_blocks,
-                               step.partition, sink.data_ptr(), strm):
+                               step.auto_partition, sink.data_ptr(), strm):
             raise SystemExit("paged probe launch failed")
 
     warm_up(stream, 3)
@@ -263,7 +268,7 @@ def time_probes(step: Step, calls: int = 20, stream_bytes: int = 2 << 30):
     return {"stream_GBps": round(stream_bytes / (ms_stream * 1e-3) / 1e9, 1),
             "stream_bytes": stream_bytes, "stream_us": round(ms_stream * 1e3, 2),
             "paged_GBps": round(kvb / (ms_paged * 1e-3) / 1e9, 1),
-            "paged_us": round(ms_paged * 1e3, 2), "paged_partition": step.partition,
+            "paged_us": round(ms_paged * 1e3, 2), "paged_partition": step.auto_partition,
             "what": "compute-free reads: a contiguous buffer, and the step's K/V rows "
                     "through its block tables in the decode's partition (plain split grid)"}
 
@@ -409,13 +414,14 @@ def time_decode_rotating(cfg: int, calls_per_set: int = 10, wl=None):
     out = torch.empty_like(q)
     max_ctx = int(wl.context_lens.max())
     part = pkv.decode_partition(wl.num_seqs, max_ctx, k_pool)
+    schedule = pkv.decode_schedule(wl.num_seqs, wl.num_q_heads, max_ctx, k_pool)
     ws = torch.zeros(max(16, pkv.decode_workspace_bytes(wl.num_seqs, wl.num_q_heads, max_ctx,
-                                                        k_pool, part)),
+                                                        k_pool)),
                      dtype=torch.uint8, device=DEV)
 
     # one prepared call per block set (arguments checked and marshalled once)
     preps = [pkv.prepare_decode(q, k_pool, v_pool, tb, ctx, wl.scale, max_ctx, out=out,
-                                partition=part, workspace=ws) for tb in tables]
+                                workspace=ws) for tb in tables]
 
     def call(i):
         preps[i]()
@@ -444,7 +450,7 @@ def time_decode_rotating(cfg: int, calls_per_set: int = 10, wl=None):
     t0 = time.perf_counter()
     for r in range(n):
         pkv.decode(q, k_pool, v_pool, tables[r % sets], ctx, wl.scale, max_ctx, out=out,
-                   partition=part, workspace=ws)
+                   workspace=ws)
     host_plain_us = (time.perf_counter() - t0) / n * 1e6
     torch.cuda.synchronize()
     loops = [ms] + [timed_loop(rotating, n) for _ in range(2)]
@@ -486,6 +492,7 @@ def time_decode_rotating(cfg: int, calls_per_set: int = 10, wl=None):
         raise SystemExit(f"{wl.name}: graph replay differs from the eager calls")
     kvb = wl.kv_bytes_per_call()
     return {"name": wl.name, "workload": workload_label(wl), "partition": part,
+            "schedule": schedule,
             "rotating_sets": sets,
             "us_per_call": round(ms * 1e3, 2), "repeats": repeat_stats(loops), "kv_bytes": kvb,
             "kv_read_GBps": round(kvb / (ms * 1e-3) / 1e9, 1),
@@ -553,9 +560,8 @@ def time_shared(name: str, calls_per_set: int = 20, partition: int = 0):
     ws_s = torch.zeros(max(16, pkv.decode_shared_workspace_bytes(
         wl.num_seqs, wl.num_q_heads, max_ctx, G, mg, mp, max_tail, k_pool, partition)),
         dtype=torch.uint8, device=DEV)
-    part = pkv.decode_partition(wl.num_seqs, max_ctx, k_pool)
     ws_p = torch.zeros(max(16, pkv.decode_workspace_bytes(wl.num_seqs, wl.num_q_heads, max_ctx,
-                                                          k_pool, part)),
+                                                          k_pool)),
                        dtype=torch.uint8, device=DEV)
     gs_d, pl_d = to_dev(gs), to_dev(pl)
 
@@ -564,8 +570,7 @@ def time_shared(name: str, calls_per_set: int = 20, partition: int = 0):
                           max_tail_len=max_tail, out=out, partition=partition, workspace=ws_s)
 
     def plain(tb):
-        pkv.decode(q, k_pool, v_pool, tb, ctx, wl.scale, max_ctx, out=out, partition=part,
-                   workspace=ws_p)
+        pkv.decode(q, k_pool, v_pool, tb, ctx, wl.scale, max_ctx, out=out, workspace=ws_p)
 
     def timed(fn):
         """(eager ms per call, ms per call replayed from one captured graph);
@@ -663,7 +668,9 @@ def time_layer_graph(cfg: int, layers: int = 16, steps: int = 20):
     st.capture()
     ms_graph = timed(st.replay)
     kvb = wl.kv_bytes_per_call() * L
-    return {"workload": workload_label(wl) + f", {L} layers", "partition": st.partition,
+    return {"workload": workload_label(wl) + f", {L} layers",
+            "schedule": pkv.decode_schedule(S, wl.num_q_heads, int(wl.context_lens.max()),
+                                            kp[0], st.partition),
             "launches_per_step": L, "eager_us": round(ms_eager * 1e3, 2),
             "graph_us": round(ms_graph * 1e3, 2), "speedup": round(ms_eager / ms_graph, 3),
             "graph_us_per_layer": round(ms_graph * 1e3 / L, 2),
@@ -857,7 +864,7 @@ def phase_trace(cfg: int):
     wl = make_workload(cfg)
     st = Step(wl)
     desc = pkv.pool_desc(st.k_pool)
-    part = L.pkv_decode_partition(wl.num_seqs, st.max_ctx, ctypes.byref(desc))
+    part = 0   # the library's automatic cut, as the bench's timed calls use
     ws = torch.zeros(max(16, L.pkv_decode_workspace_bytes(wl.num_seqs, wl.num_q_heads,
                                                           st.max_ctx, part, ctypes.byref(desc))),
                      dtype=torch.uint8, device=DEV)
@@ -913,7 +920,8 @@ def phase_trace(cfg: int):
     bins = np.arange(0.0, end.max() + step_us, step_us)
     merged = t[:, 9] == 1
     return {"workload": workload_label(wl), "call": "pkv_decode_step" if fused else "pkv_decode",
-            "partition": part, "workgroups": int(len(t)), "phases": phases,
+            "partition": st.auto_partition, "schedule": st.schedule,
+            "workgroups": int(len(t)), "phases": phases,
             "workgroup_total_us": {"mean": round(float((end - start).mean()), 2),
                                    "p50": round(float(np.median(end - start)), 2),
                                    "p90": round(float(np.percentile(end - start, 90)), 2)},
@@ -1109,7 +1117,8 @@ def main():
     pkv.load()
     step = Step(wl, args.partition)
     print(f"[bench] timing {args.steps} steps (warmup {args.warmup}, at least "
-          f"{MIN_WARMUP_S} s), partition {step.partition}", file=sys.stderr, flush=True)
+          f"{MIN_WARMUP_S} s), partition {step.auto_partition}, schedule {step.schedule}",
+          file=sys.stderr, flush=True)
     ms_step, ms_bracketed, pct_launch, reps, nwarm = time_steps(step, args.steps, args.warmup)
     cold = time_cold(step.run)
     print("[bench] read-bandwidth probes", file=sys.stderr, flush=True)
@@ -1137,7 +1146,7 @@ def main():
         "data": "synthetic N(0,1) K/V/q at the model's per-layer shape, seeded",
         "config": {"workload": workload_label(wl), "num_seqs": wl.num_seqs,
                    "total_context_tokens": wl.total_ctx, "kv_bytes_per_step": kvb,
-                   "partition_tokens": step.partition,
+                   "partition_tokens": step.auto_partition, "schedule": step.schedule,
                    "step": "pkv_decode_step: slot mapping + KV write of 1 token/seq + split "
                            "decode + merge of the splits, one launch"},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),

@@ -140,7 +140,16 @@ pkv_status pkv_write(const void* k, const void* v, const int32_t* slot_mapping,
  * piece, a longer one becomes one tail piece of its own (shorter than a
  * partition); the launch runs all full pieces first, then
  * the tail pieces, longer ones first (near-equal pieces keep every workgroup
- * stream of the GPU equally loaded and the last pieces short). Each piece of
+ * stream of the GPU equally loaded and the last pieces short). With
+ * partition 0, when a tile lies within one block and the contexts are long
+ * (num_seqs * num_kv_heads * max_context_len rows of K and V average at least
+ * 1 MiB over two workgroups per CU), pkv_decode and pkv_decode_step cut
+ * instead each KV head's sequences, laid end to end (each non-empty one
+ * preceded by 128 tokens that stand for a piece's fixed cost), into one
+ * range per workgroup, two workgroups per CU, each range at least the
+ * automatic partition long; a workgroup runs the parts of every sequence its
+ * range touches, one after another (pkv_decode_schedule tells which cut a
+ * call uses). Each piece of
  * a sequence with more than one yields a partial (running max m in log2
  * units, exp-sum l, unnormalised o) in `workspace`;
  * the last workgroup of a (sequence, KV head) to finish merges them in the
@@ -174,6 +183,19 @@ int32_t pkv_decode_partition(int32_t num_seqs, int32_t max_context_len,
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                   int32_t max_context_len, int32_t partition,
                                   const pkv_pool_desc* pool);
+
+/* Which cut pkv_decode and pkv_decode_step use for these sizes (the
+ * two-phase entry points never use stream-K ranges): PKV_SCHED_GRID (one
+ * workgroup per split of `partition` tokens of every sequence),
+ * PKV_SCHED_PIECES (the piece schedule), PKV_SCHED_LONGEST_FIRST (one piece
+ * per sequence, longest first), PKV_SCHED_STREAM_K (ranges of the laid-end-
+ * to-end sequences); -1 when the sizes are invalid (see pkv_last_error). */
+#define PKV_SCHED_GRID 0
+#define PKV_SCHED_PIECES 1
+#define PKV_SCHED_LONGEST_FIRST 2
+#define PKV_SCHED_STREAM_K 3
+int32_t pkv_decode_schedule(int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                            int32_t partition, const pkv_pool_desc* pool);
 
 pkv_status pkv_decode(const void* q, int32_t num_seqs, int32_t num_q_heads,
                       const void* k_pool, const void* v_pool,

@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     PkvError,
     PreparedCall,
     PoolDesc,
+    SCHEDULES,
     VALIDATE_FIELDS,
     abi_version,
     block_bytes,
@@ -22,6 +23,7 @@ from ._binding import (  # noqa: F401
     decode_step,
     decode_step_noalloc,
     decode_partition,
+    decode_schedule,
     decode_workspace_bytes,
     debug_enabled,
     load,

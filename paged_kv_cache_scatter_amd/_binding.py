@@ -26,7 +26,7 @@ _STATUS = {0: "PKV_OK", 1: "PKV_ERR_NULL", 2: "PKV_ERR_DTYPE", 3: "PKV_ERR_SHAPE
 
 # Every symbol include/pkv.h declares.
 EXPORTS = ("pkv_slot_mapping", "pkv_write", "pkv_decode_partition",
-           "pkv_decode_workspace_bytes", "pkv_decode", "pkv_decode_partials",
+           "pkv_decode_workspace_bytes", "pkv_decode_schedule", "pkv_decode", "pkv_decode_partials",
            "pkv_decode_reduce", "pkv_decode_step", "pkv_decode_step_partials",
            "pkv_decode_step_noalloc",
            "pkv_decode_shared_workspace_bytes", "pkv_decode_shared", "pkv_prefill",
@@ -71,6 +71,8 @@ def load(path: str | None = None):
     lib.pkv_decode_partition.restype = _I
     lib.pkv_decode_workspace_bytes.argtypes = [_I, _I, _I, _I, ctypes.POINTER(PoolDesc)]
     lib.pkv_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.pkv_decode_schedule.argtypes = [_I, _I, _I, _I, ctypes.POINTER(PoolDesc)]
+    lib.pkv_decode_schedule.restype = _I
     dec_args = [_P, _I, _I, _P, _P, ctypes.POINTER(PoolDesc), _P, _I, _P, _I, ctypes.c_float,
                 _I, _P, _P, ctypes.c_size_t, _P]
     for name in ("pkv_decode", "pkv_decode_partials", "pkv_decode_reduce"):
@@ -243,6 +245,21 @@ def decode_partition(num_seqs: int, max_context_len: int, k_pool: torch.Tensor) 
     desc = pool_desc(k_pool)
     return int(load().pkv_decode_partition(int(num_seqs), int(max_context_len),
                                            ctypes.byref(desc)))
+
+
+# pkv_decode_schedule's values (PKV_SCHED_* of include/pkv.h)
+SCHEDULES = {0: "grid", 1: "pieces", 2: "longest_first", 3: "stream_k"}
+
+
+def decode_schedule(num_seqs: int, num_q_heads: int, max_context_len: int,
+                    k_pool: torch.Tensor, partition: int = 0) -> str:
+    """The cut pkv_decode / pkv_decode_step use for these sizes (a SCHEDULES name)."""
+    desc = pool_desc(k_pool)
+    r = int(load().pkv_decode_schedule(int(num_seqs), int(num_q_heads), int(max_context_len),
+                                       int(partition), ctypes.byref(desc)))
+    if r < 0:
+        raise PkvError(3, load().pkv_last_error().decode())   # PKV_ERR_SHAPE
+    return SCHEDULES[r]
 
 
 def decode_workspace_bytes(num_seqs: int, num_q_heads: int, max_context_len: int,

@@ -21,6 +21,17 @@ thread_local char g_err[512] = "";
 constexpr int kMaxPartition = 8192;   // tokens per split (bounds the LDS table slice)
 constexpr int kMaxSplits = 4096;      // splits per sequence (bounds the merge kernel's LDS)
 constexpr int64_t kSchedMinPieceBytes = 128 << 10;   // K+V bytes of a piece worth a lookup
+// Stream-K ranges (DecodeArgs::sched_sk): two workgroups per CU, so that
+// every CU holds two equal ranges; a piece is charged 128 tokens of cost;
+// used when, at the largest contexts, a range would average at least 1 MiB of
+// K/V. Measured on the LLaMA-2-70B layer step (A/B on one box, 5 interleaved
+// rounds): 134.5 us with the piece schedule, 128.3 with equal ranges, 124.5
+// with the 128-token charge (64: 125.4, 256: 125.6, 512: 133.8); with equal
+// ranges, one workgroup per CU 175, 1.5: 156, 2.5: 152, 3: 144 us. Its TP=8
+// shard (86 MB, 1 KV head) stays on 256-token pieces: 30.2 against 39.6 us.
+constexpr int kSkWgPerCu = 2;
+constexpr int kSkAlphaTokens = 128;
+constexpr int64_t kSkMinWgBytes = 1 << 20;
 // Merge counters: a fixed area at the start of every workspace, so that calls
 // of any size sharing one buffer never write partials where another counts.
 // Launches with more (sequence, KV head) pairs merge in a second kernel.
@@ -70,6 +81,9 @@ struct DecodePlan {
   int sched_q = 0;      // small piece of the piece schedule (0: plain split grid)
   int sched_align = 0;
   bool sched_lpt = false;   // one piece per sequence, longest-first
+  int sched_sk = 0;         // > 0: stream-K ranges, workgroups per KV head
+  int sk_min_units = 0;
+  int sk_alpha = 0;
   int pair_rep = 0;         // > 0: KV heads read in pairs (real group size)
   pkv_pool_desc view{};     // the pool as the kernels read it
   size_t ws_ml_offset = 0;   // partial (m, l) pairs, after the counter area
@@ -134,7 +148,8 @@ bool pair_heads(const pkv_pool_desc* pool, int num_seqs, int rep) {
 
 pkv_status plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
                        int32_t max_ctx, int32_t partition, const pkv_pool_desc* pool,
-                       DecodePlan* plan, bool allow_sched = true, bool allow_pair = true) {
+                       DecodePlan* plan, bool allow_sched = true, bool allow_pair = true,
+                       bool allow_sk = false) {
   pkv_status st = check_pool(pool);
   if (st != PKV_OK) return st;
   if (num_seqs < 0 || num_q_heads < 1 || max_ctx < 0 || max_blocks < 1) {
@@ -215,6 +230,31 @@ pkv_status plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks
   // the longest context)
   plan->sched_lpt = plan->splits == 1 && allow_sched && num_seqs <= kSchedMaxSeqs &&
                     (int64_t)max_ctx * row_bytes >= kSchedMinPieceBytes;
+  // Stream-K ranges in place of the pieces, for an automatic partition of a
+  // launch that merges in place, when the kernel reads block ids uniformly
+  // (a tile within one block) and the ranges are long. The partition is the
+  // least range (a bound on the partial slots a sequence can need).
+  plan->sched_sk = plan->sk_min_units = plan->sk_alpha = 0;
+  const int A = plan->view.block_size;
+  const int heads = plan->view.num_kv_heads;
+  const int64_t wgs = (int64_t)kSkWgPerCu * num_cus();
+  const int64_t units = ((int64_t)max_ctx + A - 1) / A;
+  const int alpha = std::max(1, kSkAlphaTokens / A);
+  if (allow_sk && partition == 0 && plan->sched_q > 0 && A >= align && wgs >= heads &&
+      (int64_t)num_seqs * heads <= (int64_t)kMergeCounters &&
+      (int64_t)num_seqs * (units + alpha) < (1ll << 30) &&
+      (int64_t)num_seqs * heads * max_ctx * row_bytes >= kSkMinWgBytes * wgs) {
+    const int mu = std::max(1, part / A);
+    const int64_t J = (units + mu - 1) / mu + 1;
+    if (J <= kMaxSplits) {
+      plan->sched_sk = (int)(wgs / heads);
+      plan->sk_min_units = mu;
+      plan->sk_alpha = alpha;
+      plan->sched_q = 0;
+      plan->sched_align = A;
+      plan->splits = (int)J;
+    }
+  }
   plan->ws_ml_offset = plan->ws_o_offset = plan->ws_bytes = 0;
   if (plan->splits > 1) plan_workspace(num_seqs, num_q_heads, &plan->view, plan->splits, plan);
   return PKV_OK;
@@ -314,7 +354,7 @@ pkv_status decode_impl(Phase phase, const void* q, int32_t num_seqs, int32_t num
   pkv_status st = shared ? plan_shared(num_seqs, num_q_heads, max_blocks, max_ctx, *shared,
                                        partition, pool, &plan, &sd)
                          : plan_decode(num_seqs, num_q_heads, max_blocks, max_ctx, partition,
-                                       pool, &plan);
+                                       pool, &plan, true, true, phase == Phase::kBoth);
   if (st != PKV_OK) return st;
   if (num_seqs == 0) return PKV_OK;
   if (shared && shared->num_groups > 0 && (!shared->group_start || !shared->prefix_lens)) {
@@ -374,6 +414,9 @@ pkv_status decode_impl(Phase phase, const void* q, int32_t num_seqs, int32_t num
   a.sched_q = plan.sched_q;
   a.sched_align = plan.sched_align;
   a.sched_lpt = plan.sched_lpt;
+  a.sched_sk = plan.sched_sk;
+  a.sk_min_units = plan.sk_min_units;
+  a.sk_alpha = plan.sk_alpha;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.cu_q = nullptr;
   a.total_q = 0;
@@ -606,7 +649,28 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
   if (plan_decode(num_seqs, num_q_heads, maxb > 0 ? maxb : 1, max_context_len, partition,
                   pool, &plan) != PKV_OK)
     return 0;
-  return plan.ws_bytes;
+  // one size for every entry point: the in-launch plan may use stream-K ranges
+  DecodePlan in_launch;
+  if (plan_decode(num_seqs, num_q_heads, maxb > 0 ? maxb : 1, max_context_len, partition,
+                  pool, &in_launch, true, true, true) != PKV_OK)
+    return 0;
+  return std::max(plan.ws_bytes, in_launch.ws_bytes);
+}
+
+int32_t pkv_decode_schedule(int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                            int32_t partition, const pkv_pool_desc* pool) {
+  if (!pool) return -1;
+  DecodePlan plan;
+  const int32_t maxb = pool->block_size > 0
+                           ? (max_context_len + pool->block_size - 1) / pool->block_size
+                           : 1;
+  if (plan_decode(num_seqs, num_q_heads, maxb > 0 ? maxb : 1, max_context_len, partition,
+                  pool, &plan, true, true, true) != PKV_OK)
+    return -1;
+  if (plan.sched_sk > 0) return PKV_SCHED_STREAM_K;
+  if (plan.sched_q > 0) return PKV_SCHED_PIECES;
+  if (plan.sched_lpt) return PKV_SCHED_LONGEST_FIRST;
+  return PKV_SCHED_GRID;
 }
 
 pkv_status pkv_decode(const void* q, int32_t num_seqs, int32_t num_q_heads, const void* k_pool,
@@ -701,7 +765,7 @@ pkv_status pkv_decode_step_noalloc(const void* q, const void* k_new, const void*
   // the size check comes before any device call
   DecodePlan plan;
   pkv_status st = plan_decode(num_seqs, num_q_heads, max_blocks_per_seq, max_context_len,
-                              partition, pool, &plan);
+                              partition, pool, &plan, true, true, true);
   if (st != PKV_OK) return st;
   if (plan.ws_bytes > kNoallocScratchBytes) {
     set_error("this decode step needs %zu bytes of scratch; the library's fixed area holds "

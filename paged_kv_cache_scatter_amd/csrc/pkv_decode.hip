@@ -1022,6 +1022,54 @@ __device__ __forceinline__ bool find_sequence_lpt(const DecodeArgs& a, int pid, 
   return pc.s >= 0;
 }
 
+// Stream-K layout of one KV head's stream (see DecodeArgs::sched_sk): every
+// thread takes four consecutive sequences, a workgroup scan of their unit
+// counts (a non-empty sequence costs sk_alpha + ceil(L / A) units) gives
+// st[s], the unit where sequence s's tokens start, and len[s], its clamped
+// length. Returns the stream's total units. `tmp` holds kWaves ints; the
+// caller's later reads of st and len follow the barrier at the end.
+__device__ __forceinline__ int sk_layout(const DecodeArgs& a, int lim, int* st, int* len,
+                                         int* tmp) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int la = __builtin_ctz((unsigned)a.sched_align);
+  int L[4];
+  uint32_t u[4], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {   // all four loads in flight together
+    const int sq = tid * 4 + i;
+    L[i] = sq < a.num_seqs ? a.ctx_lens[sq] : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    L[i] = L[i] < 0 ? 0 : (L[i] > lim ? lim : L[i]);
+    u[i] = ((uint32_t)L[i] + (uint32_t)a.sched_align - 1u) >> la;
+    sum += u[i] ? u[i] + (uint32_t)a.sk_alpha : 0u;
+  }
+  const uint32_t incl = wave_incl_scan(sum);
+  if (lane == 63) tmp[w] = (int)incl;
+  __syncthreads();
+  uint32_t base = 0, total = 0;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) {
+    const uint32_t v = (uint32_t)tmp[k];
+    if (k < w) base += v;
+    total += v;
+  }
+  uint32_t at = base + incl - sum;   // this thread's first sequence's cost starts here
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int sq = tid * 4 + i;
+    const uint32_t pad = u[i] ? (uint32_t)a.sk_alpha : 0u;
+    if (sq < a.num_seqs) {
+      st[sq] = (int)(at + pad);
+      len[sq] = L[i];
+    }
+    at += u[i] + pad;
+  }
+  __syncthreads();
+  return (int)total;
+}
+
 template <typename T, int HD, int REP, int PR>
 __global__ void __launch_bounds__(kThreads)
 decode_partials_kernel(DecodeArgs a) {
@@ -1048,8 +1096,11 @@ decode_partials_kernel(DecodeArgs a) {
   int ctx;
   // piece schedule: this workgroup's sequence, token range and partial slot
   Piece pc{};
-  const bool sched = a.sched_q > 0 || a.sched_lpt;
-  if (sched) {
+  const bool sk = a.sched_sk > 0;
+  const bool sched = a.sched_q > 0 || a.sched_lpt || sk;
+  if (sk) {
+    // the pieces come from the loop over this workgroup's range at the end
+  } else if (sched) {
     const int pid = blockIdx.y + gridDim.y * blockIdx.z;
     int* scan_lds = reinterpret_cast<int*>(smem);
     if (a.sched_lpt ? !find_sequence_lpt(a, pid, lim, pc, scan_lds)
@@ -1085,6 +1136,9 @@ decode_partials_kernel(DecodeArgs a) {
     ctx = a.ctx_lens[s];
     ctx = ctx < 0 ? 0 : (ctx > lim ? lim : ctx);
   }
+  // One piece (s, j, ctx, pc): everything from here to the end of the lambda
+  // runs once per piece; its returns end the piece.
+  auto piece = [&]() __attribute__((always_inline)) {
   // Shared-prefix decode: the group's shared pass covers positions < start
   // (nps partials in the leading slots); this kernel covers the tail.
   int start = 0, nps = 0, slot0 = 0;
@@ -1358,6 +1412,69 @@ decode_partials_kernel(DecodeArgs a) {
   __syncthreads();
   PKV_PHASE(8);
 #endif
+  };
+
+  if (!sk) {
+    piece();
+    return;
+  }
+  // ---- stream-K: the pieces of workgroup i's range [i E, (i + 1) E) of the
+  // head's stream, in sequence order. E = ceil(U / sched_sk), at least
+  // sk_min_units; the range of the last workgroup with tokens runs to the end,
+  // so that empty sequences after the last token belong to it. A sequence's
+  // tokens occupy units [a0, a1); its piece in range i is partial slot
+  // i - floor(a0 / E) of floor((a1 - 1) / E) - floor(a0 / E) + 1. An empty
+  // sequence (a0 == a1) is one piece, of the range holding a0.
+  if (!Lds<T, HD, REP>::uniform(bshift)) return;   // the planner never asks for it
+  int* st_lds = reinterpret_cast<int*>(smem + round16(Lds<T, HD, REP>::bytes(0)));
+  int* len_lds = st_lds + a.num_seqs;
+  const int U = sk_layout(a, lim, st_lds, len_lds, len_lds + a.num_seqs);
+  const int la = __builtin_ctz((unsigned)a.sched_align);
+  const int i = blockIdx.y;
+  int E = (int)(((int64_t)U + a.sched_sk - 1) / a.sched_sk);
+  E = E < a.sk_min_units ? a.sk_min_units : E;
+  const int last_active = U > 0 ? (U - 1) / E : 0;
+  if (i > last_active) return;
+  const int lo = i * E;
+  const int64_t hi = i == last_active ? INT64_MAX : (int64_t)(i + 1) * E;
+  auto units = [&](int sq) { return (len_lds[sq] + a.sched_align - 1) >> la; };
+  // first sequence with tokens past lo, or empty at or after it
+  int l = 0, r = a.num_seqs;
+  while (l < r) {
+    const int m = (l + r) >> 1;
+    if (st_lds[m] + units(m) > lo || st_lds[m] >= lo) r = m;
+    else l = m + 1;
+  }
+  for (int sq = l; sq < a.num_seqs; ++sq) {
+    const int a0 = st_lds[sq], a1 = a0 + units(sq), c = len_lds[sq];
+    if ((int64_t)a0 >= hi) break;
+    Piece p;
+    p.s = sq;
+    p.ctx = c;
+    if (a1 == a0) {
+      p.t0 = p.t1 = 0;
+      p.slot = 0;
+      p.n = 1;
+    } else {
+      const int b0 = a0 > lo ? a0 : lo;
+      const int b1 = (int64_t)a1 < hi ? a1 : (int)hi;
+      const int e1 = (b1 - a0) << la;
+      p.t0 = (b0 - a0) << la;
+      p.t1 = e1 < c ? e1 : c;
+      p.slot = i - a0 / E;
+      p.n = (a1 - 1) / E - a0 / E + 1;
+    }
+    // memory safety whatever the layout gave: an inconsistent piece does no work
+    if (p.t0 < 0 || p.t0 > p.t1 || p.t1 > p.ctx || p.ctx > lim || p.slot < 0 ||
+        p.slot >= p.n || p.n > a.num_splits)
+      continue;
+    __syncthreads();   // the previous piece is done with LDS
+    s = qrow = p.s;
+    j = p.slot;
+    ctx = p.ctx;
+    pc = p;
+    piece();
+  }
 }
 
 // Merge split partials of sequences with more than one split: one wave per
@@ -1419,10 +1536,15 @@ template <typename T, int HD, int REP, int PR = 0>
 pkv_status launch_split(const DecodeArgs& a, hipStream_t st) {
   using L = Lds<T, HD, REP>;
   const int piece = a.sched_q > 0 ? max_piece(a.partition, a.sched_q) : a.partition;
-  const int lds = L::bytes(L::table_entries(piece, a.block_shift));
+  int lds = L::bytes(L::table_entries(piece, a.block_shift));
   // shared-prefix decode: the leading slots belong to the shared pass
   dim3 grid(a.num_kv_heads, a.num_seqs, a.num_splits - a.sh.prefix_slots);
-  if (a.sched_q > 0 || a.sched_lpt) {
+  if (a.sched_sk > 0) {
+    // stream-K: sched_sk ranges per KV head; the layout (start, length per
+    // sequence, the scan's words) after the piece's LDS
+    lds = round16(L::bytes(0)) + (2 * a.num_seqs + kWaves) * (int)sizeof(int);
+    grid = dim3(a.num_kv_heads, a.sched_sk, 1);
+  } else if (a.sched_q > 0 || a.sched_lpt) {
     // pieces: at most num_splits per sequence (one in longest-first order)
     const int planes = a.num_seqs * a.num_splits;
     const int y = planes < kRowGridZ ? planes : kRowGridZ;

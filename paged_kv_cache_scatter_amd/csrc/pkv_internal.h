@@ -111,6 +111,18 @@ struct DecodeArgs {
   // sequences): the grid's (y, z) plane enumerates the sequences by length
   // class, longest class first (kLenClasses classes of the length range).
   int32_t sched_lpt;
+  // Stream-K ranges (sched_sk > 0: workgroups per KV head; no shared prefix,
+  // no prefill rows, in-launch merge, a uniform-id kernel, at most
+  // kSchedMaxSeqs sequences): each KV head's sequences are laid end to end
+  // as one stream of sched_align-token units, every non-empty sequence
+  // preceded by sk_alpha units that stand for the fixed cost of a piece
+  // (they hold no tokens). The stream is cut into sched_sk equal ranges of
+  // at least sk_min_units units; workgroup i of a head runs, one after
+  // another, the pieces of every sequence its range touches. Piece k of a
+  // sequence is its part in the k-th range it touches (its partial slot k).
+  int32_t sched_sk;
+  int32_t sk_min_units;
+  int32_t sk_alpha;
   // Paired KV heads (> 0: the group size of the real heads): the pool is read
   // as num_kv_heads virtual heads of two adjacent real heads each (rows of
   // 2 * head_dim, the same bytes), a workgroup serving both groups' query

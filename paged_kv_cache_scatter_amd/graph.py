@@ -42,7 +42,8 @@ class LayerSteps:
         self.tables, self.ctx = tables, context_lens
         self.scale, self.max_ctx = float(scale), int(max_context_len)
         S, Hq = q.shape[1], q.shape[2]
-        self.partition = partition or _b.decode_partition(S, self.max_ctx, k_pools[0])
+        # 0 leaves the cut to the library (it may then use stream-K ranges)
+        self.partition = int(partition)
         nws = _b.decode_workspace_bytes(S, Hq, self.max_ctx, k_pools[0], self.partition)
         # one workspace serves every layer: the layers run in stream order
         self.ws = torch.zeros(max(nws, 16), dtype=torch.uint8, device=q.device)

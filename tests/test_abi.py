@@ -221,6 +221,37 @@ def test_piece_schedule_needs_large_pieces(lib):
     assert slots(1024) == 4096 // 1024 + 1
 
 
+def test_decode_schedule_choice(lib):
+    """pkv_decode_schedule: with partition 0, the 70B layer shape (64
+    sequences, 8 KV heads of 128 bf16 dims, contexts up to 8192) takes the
+    stream-K ranges; its explicit automatic partition, its TP=8 shard (one KV
+    head: ranges of under 1 MiB of K/V at the largest contexts), 192
+    Llama-3.2-1B sequences (one piece each, longest first) and 8 x 2048 (the
+    plain grid) do not. The workspace size covers both cuts."""
+    d70 = _desc(nb=32769, bs=16, hkv=8, hd=128)
+    sched = lib.pkv_decode_schedule
+    assert sched(64, 64, 8192, 0, ctypes.byref(d70)) == 3
+    part = lib.pkv_decode_partition(64, 8192, ctypes.byref(d70))
+    assert part == 1024
+    assert sched(64, 64, 8192, part, ctypes.byref(d70)) == 1
+    # stream-K slots: ceil(512 units / 64) + 1 = 9, as the piece schedule's
+    rows = 64 * 64 * 9
+    assert lib.pkv_decode_workspace_bytes(64, 64, 8192, 0, ctypes.byref(d70)) == \
+        COUNTER_AREA + rows * 2 * 4 + rows * 128 * 4
+    shard = _desc(nb=32769, bs=16, hkv=1, hd=128)
+    assert sched(64, 8, 8192, 0, ctypes.byref(shard)) == 1
+    d1b = _desc(nb=32768, bs=16, hkv=8, hd=64)
+    assert sched(192, 32, 2048, 0, ctypes.byref(d1b)) == 2
+    assert sched(8, 32, 2048, 0, ctypes.byref(d1b)) == 0
+    # a tile wider than a block (bf16 head_dim 128 reads 8-token tiles) keeps the pieces
+    d_bs4 = _desc(nb=1 << 18, bs=4, hkv=8, hd=128)
+    assert sched(64, 64, 8192, 0, ctypes.byref(d_bs4)) == 1
+    # more sequences than the scan takes: the plain grid
+    assert sched(1025, 8, 4096, 0, ctypes.byref(shard)) == 0
+    assert sched(64, 60, 8192, 0, ctypes.byref(d70)) == -1 and "multiple" in _err(lib)
+    assert sched(64, 64, 8192, 0, None) == -1
+
+
 def test_partition_validity_does_not_depend_on_pairing(lib):
     """bf16 rows of 64 dims take 32-token tiles, so a partition must be a
     multiple of 32 whether or not the launch reads its KV heads in pairs

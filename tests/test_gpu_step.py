@@ -182,22 +182,28 @@ def test_step_invalid_block_for_new_token():
     check_close(out_f64(out, "f32"), ref, "f32")
 
 
-@pytest.mark.parametrize("cfg", [4, 5])
-def test_step_full_size_as_benchmarked(cfg):
+@pytest.mark.parametrize("cfg,cut", [(4, "auto"), (5, "auto"), (5, "pieces")])
+def test_step_full_size_as_benchmarked(cfg, cut):
     """The benchmark's timed call at full size: pkv_decode_step on every
-    sequence of the workload with the automatic partition and a zero-filled
-    workspace, the new token of each sequence at position ctx - 1. Both pools
-    are compared bit for bit with the oracle's bulk write followed by the
-    step's write, and every output element with the oracle's decode."""
+    sequence of the workload with partition 0 (the library's own cut: the
+    stream-K ranges for the 70B layer, longest-first single pieces for the
+    192 sequences) and a zero-filled workspace, the new token of each sequence
+    at position ctx - 1; "pieces" passes the automatic partition explicitly,
+    which keeps the piece schedule. Both pools are compared bit for bit with
+    the oracle's bulk write followed by the step's write, and every output
+    element with the oracle's decode."""
     wl = make_workload(cfg)
     rows = _new_rows(wl)
     pc = PoolCase(wl, exclude_last=True)
-    part = pkv.decode_partition(wl.num_seqs, pc.max_ctx, pc.k_pool)
+    part = 0 if cut == "auto" else pkv.decode_partition(wl.num_seqs, pc.max_ctx, pc.k_pool)
+    schedule = pkv.decode_schedule(wl.num_seqs, wl.num_q_heads, pc.max_ctx, pc.k_pool, part)
+    assert schedule == {(4, "auto"): "longest_first", (5, "auto"): "stream_k",
+                        (5, "pieces"): "pieces"}[(cfg, cut)]
     ws = torch.zeros(max(16, pkv.decode_workspace_bytes(wl.num_seqs, wl.num_q_heads,
                                                         pc.max_ctx, pc.k_pool, part)),
                      dtype=torch.uint8, device=pc.q.device)
     out = torch.empty_like(pc.q)
-    note(f"{wl.name}: full-size pkv_decode_step, partition {part}")
+    note(f"{wl.name}: full-size pkv_decode_step, partition {part or 'auto'}, {schedule}")
     pkv.decode_step(pc.q, to_dev(wl.k_rows[rows]), to_dev(wl.v_rows[rows]), pc.k_pool,
                     pc.v_pool, pc.tables, pc.ctx, wl.scale, pc.max_ctx, out=out,
                     partition=part, workspace=ws)
