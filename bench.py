@@ -229,16 +229,19 @@ PROBE_LIB = os.path.join(ROOT, "paged_kv_cache_scatter_amd", "libpkv_probe.so")
 def time_probes(step: Step, calls: int = 20, stream_bytes: int = 2 << 30):
     """Read-bandwidth probes with no arithmetic (libpkv_probe.so): a contiguous
     ``stream_bytes`` buffer read once per call with 16-byte non-temporal
-    loads, and the step's own K/V rows read through its block tables in the
-    decode's order and partition. GB/s of each (the paged probe counted in the
-    step's algorithmic K/V bytes)."""
+    loads, and the step's own K/V rows read through its block tables, one
+    workgroup per (KV head, sequence, split), over split sizes of 256, 512
+    and 1024 tokens and 1, 2 or 4 token rows per thread in flight. GB/s of
+    each (the paged probe counted in the step's algorithmic K/V bytes): the
+    paged figure at the automatic partition with one row in flight, and the
+    best of the sweep (the ceiling the decode is compared with)."""
     import ctypes
     if not os.path.exists(PROBE_LIB):
         raise SystemExit(f"{PROBE_LIB} is not built; run __graft_entry__.build()")
     lib = ctypes.CDLL(PROBE_LIB)
     P, I = ctypes.c_void_p, ctypes.c_int32
     lib.pkv_probe_stream.argtypes = [P, ctypes.c_size_t, I, P, P]
-    lib.pkv_probe_paged.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, P, P]
+    lib.pkv_probe_paged.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, I, P, P]
     wl = step.wl
     buf = torch.ones(stream_bytes // 4, dtype=torch.int32, device=DEV)
     blocks = 256 * 16
@@ -251,26 +254,41 @@ def time_probes(step: Step, calls: int = 20, stream_bytes: int = 2 << 30):
 
     row_bytes = wl.head_dim * wl.itemsize
 
-    def paged():
-        if lib.pkv_probe_paged(step.k_pool.data_ptr(), step.v_pool.data_ptr(),
-                               step.tables.data_ptr(), wl.block_tables.shape[1],
-                               step.ctx.data_ptr(), wl.num_seqs, step.max_ctx,
-                               wl.num_kv_heads, row_bytes, wl.block_size, wl.num_blocks,
-                               step.auto_partition, sink.data_ptr(), strm):
-            raise SystemExit("paged probe launch failed")
+    def paged(part, unroll):
+        def run():
+            if lib.pkv_probe_paged(step.k_pool.data_ptr(), step.v_pool.data_ptr(),
+                                   step.tables.data_ptr(), wl.block_tables.shape[1],
+                                   step.ctx.data_ptr(), wl.num_seqs, step.max_ctx,
+                                   wl.num_kv_heads, row_bytes, wl.block_size, wl.num_blocks,
+                                   part, unroll, sink.data_ptr(), strm):
+                raise SystemExit("paged probe launch failed")
+        return run
 
     warm_up(stream, 3)
     ms_stream = timed_loop(stream, calls)
-    warm_up(paged, 3)
-    ms_paged = timed_loop(paged, calls)
     del buf
     kvb = wl.kv_bytes_per_call()
+    sweep = {}
+    for part in sorted({256, 512, 1024, step.auto_partition}):
+        if part % wl.block_size:
+            continue
+        for unroll in (1, 2, 4):
+            fn = paged(part, unroll)
+            warm_up(fn, 3)
+            sweep[(part, unroll)] = timed_loop(fn, calls)
+    at_part = sweep.get((step.auto_partition, 1))
+    best = min(sweep, key=sweep.get)
     return {"stream_GBps": round(stream_bytes / (ms_stream * 1e-3) / 1e9, 1),
             "stream_bytes": stream_bytes, "stream_us": round(ms_stream * 1e3, 2),
-            "paged_GBps": round(kvb / (ms_paged * 1e-3) / 1e9, 1),
-            "paged_us": round(ms_paged * 1e3, 2), "paged_partition": step.auto_partition,
+            "paged_GBps": round(kvb / (sweep[best] * 1e-3) / 1e9, 1),
+            "paged_us": round(sweep[best] * 1e3, 2),
+            "paged_best": {"partition": best[0], "rows_in_flight": best[1]},
+            "paged_at_partition_GBps": round(kvb / (at_part * 1e-3) / 1e9, 1) if at_part else None,
+            "paged_partition": step.auto_partition,
+            "paged_sweep_us": {f"{p}x{u}": round(v * 1e3, 2) for (p, u), v in sweep.items()},
             "what": "compute-free reads: a contiguous buffer, and the step's K/V rows "
-                    "through its block tables in the decode's partition (plain split grid)"}
+                    "through its block tables (one workgroup per KV head, sequence and "
+                    "split; paged_GBps is the best split size and rows in flight)"}
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
@@ -572,6 +590,14 @@ def time_shared(name: str, calls_per_set: int = 20, partition: int = 0):
     def plain(tb):
         pkv.decode(q, k_pool, v_pool, tb, ctx, wl.scale, max_ctx, out=out, workspace=ws_p)
 
+    # plain decode with the automatic partition passed explicitly (the piece
+    # schedule where the default would take stream-K ranges)
+    part = pkv.decode_partition(wl.num_seqs, max_ctx, k_pool)
+
+    def plain_pieces(tb):
+        pkv.decode(q, k_pool, v_pool, tb, ctx, wl.scale, max_ctx, out=out, partition=part,
+                   workspace=ws_p)
+
     def timed(fn):
         """(eager ms per call, ms per call replayed from one captured graph);
         the eager figure holds the binding's host time when a call is short.
@@ -612,6 +638,8 @@ def time_shared(name: str, calls_per_set: int = 20, partition: int = 0):
         return eager, e0.elapsed_time(e1) / (3 * calls)
 
     eager_plain, ms_plain = timed(plain)
+    schedule = pkv.decode_schedule(wl.num_seqs, wl.num_q_heads, max_ctx, k_pool)
+    ms_pieces = timed(plain_pieces)[1] if schedule == "stream_k" else ms_plain
     eager_shared, ms_shared = timed(shared)
     kv_plain = wl.kv_bytes_per_call()                 # every sequence reads its whole context
     kv_unique = (int(pl.sum()) + sum(tails)) * row_b  # each prompt once, each tail once
@@ -621,8 +649,11 @@ def time_shared(name: str, calls_per_set: int = 20, partition: int = 0):
             "rotating_sets": sets, "total_context_tokens": wl.total_ctx,
             "timing": "graph replay (device time per call); eager_* include the binding's "
                       "host time",
-            "plain_us": round(ms_plain * 1e3, 2), "shared_us": round(ms_shared * 1e3, 2),
+            "plain_us": round(ms_plain * 1e3, 2), "plain_schedule": schedule,
+            "plain_pieces_us": round(ms_pieces * 1e3, 2),
+            "shared_us": round(ms_shared * 1e3, 2),
             "speedup": round(ms_plain / ms_shared, 3),
+            "speedup_vs_faster_plain": round(min(ms_plain, ms_pieces) / ms_shared, 3),
             "eager_plain_us": round(eager_plain * 1e3, 2),
             "eager_shared_us": round(eager_shared * 1e3, 2),
             "plain_kv_bytes": kv_plain, "shared_unique_kv_bytes": kv_unique,
@@ -841,7 +872,9 @@ PHASES = ["entry", "piece and context length known", "queries and block ids arri
 def phase_trace(cfg: int):
     """One launch of the decode (config 5: the fused step) through the traced
     build (libpkv_trace.so: the same kernels recording the 100 MHz realtime
-    counter at each phase boundary of every workgroup), after warm-up and a
+    counter at each phase boundary of every workgroup; a workgroup that runs
+    several pieces keeps the phases of its first and the end of its last, and
+    counts them), after warm-up and a
     512 MiB cache-evicting write. Returns per-phase durations over the
     workgroups, the launch's timeline and how many workgroups are alive over
     it. The traced kernel waits for each timestamp, so it runs a little slower
@@ -888,7 +921,7 @@ def phase_trace(cfg: int):
             raise SystemExit(f"traced call failed with status {r}")
 
     warm_up(call, 200)
-    rows, cols = 1 << 16, 10
+    rows, cols = 1 << 16, 11
     buf = np.zeros((rows, cols), dtype=np.uint64)
     scratch = torch.empty(COLD_FLUSH_BYTES, dtype=torch.uint8, device=DEV)
     scratch.fill_(1)
@@ -919,6 +952,9 @@ def phase_trace(cfg: int):
     step_us = 2.0 if end.max() < 60 else 5.0
     bins = np.arange(0.0, end.max() + step_us, step_us)
     merged = t[:, 9] == 1
+    npieces = t[:, 10]
+    one = merged & (npieces <= 1)   # the merge is the last phase of a one-piece workgroup
+    counts = {int(k): int((npieces == k).sum()) for k in np.unique(npieces)}
     return {"workload": workload_label(wl), "call": "pkv_decode_step" if fused else "pkv_decode",
             "partition": st.auto_partition, "schedule": st.schedule,
             "workgroups": int(len(t)), "phases": phases,
@@ -929,9 +965,10 @@ def phase_trace(cfg: int):
             "last_end_us": round(float(end.max()), 2),
             "first_kv_in_lds_us": {"min": round(float(first.min()), 2),
                                    "p50": round(float(np.median(first)), 2)},
+            "pieces_per_workgroup": counts,
             "merging_workgroups": int(merged.sum()),
-            "merge_us_mean": round(float(us(t[merged, 8] - t[merged, 7]).mean()), 2)
-            if merged.any() else None,
+            "merge_us_mean": round(float(us(t[one, 8] - t[one, 7]).mean()), 2)
+            if one.any() else None,
             "alive_bin_us": step_us,
             "alive": [int(((start <= b) & (end > b)).sum()) for b in bins]}
 
@@ -940,7 +977,7 @@ def phase_trace(cfg: int):
 # that decide what its launches read and write (the kernel, the planner or
 # launcher that sizes them, and their shared header).
 COUNTED = {
-    "decode": ("decode_partials_kernel<unsigned short, 128, 8, 0>", COUNTERS,
+    "decode": ("decode_partials_kernel<unsigned short, 128, 8, 0, true>", COUNTERS,
                ("pkv_decode.hip", "pkv_api.hip", "pkv_internal.h")),
     "write": ("write_kernel", WRITE_COUNTERS, ("pkv_write.hip", "pkv_api.hip", "pkv_internal.h")),
 }
@@ -1152,7 +1189,8 @@ def main():
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(wl.num_seqs / (ms_step * 1e-3), 1),
         "context_tokens_per_s": round(wl.total_ctx / (ms_step * 1e-3), 1),
-        "roofline": {"bound": "hbm", "kernel": "decode_partials_kernel (fused step)",
+        "roofline": {"bound": "hbm",
+                     "kernel": f"decode_partials_kernel (fused step, {step.schedule} cut)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "pct_of_stream_probe": round(achieved / probe["stream_GBps"], 4),

@@ -232,7 +232,8 @@ pkv_status plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks
                     (int64_t)max_ctx * row_bytes >= kSchedMinPieceBytes;
   // Stream-K ranges in place of the pieces, for an automatic partition of a
   // launch that merges in place, when the kernel reads block ids uniformly
-  // (a tile within one block) and the ranges are long. The partition is the
+  // (a tile within one block), its rows are unpaired and of 256 bytes or more
+  // (the compiled stream-K variants) and the ranges are long. The partition is the
   // least range (a bound on the partial slots a sequence can need).
   plan->sched_sk = plan->sk_min_units = plan->sk_alpha = 0;
   const int A = plan->view.block_size;
@@ -241,6 +242,7 @@ pkv_status plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks
   const int64_t units = ((int64_t)max_ctx + A - 1) / A;
   const int alpha = std::max(1, kSkAlphaTokens / A);
   if (allow_sk && partition == 0 && plan->sched_q > 0 && A >= align && wgs >= heads &&
+      plan->pair_rep == 0 && plan->view.head_dim * dtype_bytes(pool->dtype) >= 256 &&
       (int64_t)num_seqs * heads <= (int64_t)kMergeCounters &&
       (int64_t)num_seqs * (units + alpha) < (1ll << 30) &&
       (int64_t)num_seqs * heads * max_ctx * row_bytes >= kSkMinWgBytes * wgs) {

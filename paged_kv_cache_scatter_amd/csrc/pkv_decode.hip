@@ -42,34 +42,9 @@ namespace {
 
 using namespace dev;
 
-// Phase timestamps (the benchmark's traced build, libpkv_trace.so, compiled
-// with PKV_PHASE_TRACE): wave 0 of each workgroup records the 100 MHz
-// realtime counter at the phase boundaries of the decode kernel into one row
-// per linear workgroup id. Phases: 0 entry, 1 piece and context length known,
-// 2 queries and block ids arrived, 3 first K/V tile in LDS, 4 tiles done,
-// 5 partial stored, 6 stores acknowledged, 7 counted, 8 end; slot 9 is 1 for
-// the workgroup that merged. The normal build compiles all of this away.
-#ifdef PKV_PHASE_TRACE
-constexpr int kTraceRows = 1 << 16, kTraceCols = 10;
-__device__ unsigned long long g_phase_trace[kTraceRows][kTraceCols];
-__device__ __forceinline__ unsigned long long phase_clock() {
-  unsigned long long t;
-  asm volatile("s_memrealtime %0\n\ts_waitcnt lgkmcnt(0)" : "=s"(t) :: "memory");
-  return t;
-}
-__device__ __forceinline__ void phase_set(int i, unsigned long long v) {
-  // a wave-uniform condition, so that no scalar value becomes divergent
-  if (__builtin_amdgcn_readfirstlane(threadIdx.x) < 64) {
-    const int w = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-    if (w < kTraceRows) g_phase_trace[w][i] = v;
-  }
-}
-#define PKV_PHASE(i) phase_set((i), phase_clock())
-#define PKV_PHASE_VALUE(i, v) phase_set((i), (unsigned long long)(v))
-#else
-#define PKV_PHASE(i) do { } while (0)
-#define PKV_PHASE_VALUE(i, v) do { } while (0)
-#endif
+// Phase timestamps of the benchmark's traced build (PKV_PHASE, PKV_PHASE_VALUE;
+// nothing in the normal build).
+#include "pkv_phase_trace.h"
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
@@ -1070,7 +1045,9 @@ __device__ __forceinline__ int sk_layout(const DecodeArgs& a, int lim, int* st, 
   return (int)total;
 }
 
-template <typename T, int HD, int REP, int PR>
+// SK: the stream-K variant (DecodeArgs::sched_sk), compiled for rows of 256
+// bytes or more only; the other variant runs one piece per workgroup.
+template <typename T, int HD, int REP, int PR, bool SK>
 __global__ void __launch_bounds__(kThreads)
 decode_partials_kernel(DecodeArgs a) {
   using G = Geo<T, HD, REP>;
@@ -1096,9 +1073,8 @@ decode_partials_kernel(DecodeArgs a) {
   int ctx;
   // piece schedule: this workgroup's sequence, token range and partial slot
   Piece pc{};
-  const bool sk = a.sched_sk > 0;
-  const bool sched = a.sched_q > 0 || a.sched_lpt || sk;
-  if (sk) {
+  const bool sched = a.sched_q > 0 || a.sched_lpt || SK;
+  if (SK) {
     // the pieces come from the loop over this workgroup's range at the end
   } else if (sched) {
     const int pid = blockIdx.y + gridDim.y * blockIdx.z;
@@ -1414,10 +1390,9 @@ decode_partials_kernel(DecodeArgs a) {
 #endif
   };
 
-  if (!sk) {
+  if constexpr (!SK) {
     piece();
-    return;
-  }
+  } else {
   // ---- stream-K: the pieces of workgroup i's range [i E, (i + 1) E) of the
   // head's stream, in sequence order. E = ceil(U / sched_sk), at least
   // sk_min_units; the range of the last workgroup with tokens runs to the end,
@@ -1474,6 +1449,7 @@ decode_partials_kernel(DecodeArgs a) {
     ctx = p.ctx;
     pc = p;
     piece();
+  }
   }
 }
 
@@ -1553,7 +1529,17 @@ pkv_status launch_split(const DecodeArgs& a, hipStream_t st) {
     const int z = a.total_q < kRowGridZ ? a.total_q : kRowGridZ;
     grid = dim3(a.num_kv_heads, (a.total_q + z - 1) / z, z);
   }
-  hipLaunchKernelGGL((decode_partials_kernel<T, HD, REP, PR>), grid, dim3(kThreads), lds, st, a);
+  if (a.sched_sk > 0) {
+    if constexpr (PR == 0 && HD * sizeof(T) >= 256) {
+      hipLaunchKernelGGL((decode_partials_kernel<T, HD, REP, PR, true>), grid, dim3(kThreads),
+                         lds, st, a);
+      return launch_status("decode_partials_kernel");
+    }
+    set_error("stream-K ranges are compiled for unpaired rows of 256 bytes or more only");
+    return PKV_ERR_UNSUPPORTED;
+  }
+  hipLaunchKernelGGL((decode_partials_kernel<T, HD, REP, PR, false>), grid, dim3(kThreads), lds,
+                     st, a);
   return launch_status("decode_partials_kernel");
 }
 

@@ -6,7 +6,8 @@
 //  * paged:  the K and V rows of every (sequence, KV head) read through the
 //            block table in the decode's order (one workgroup per (KV head,
 //            sequence, split of `partition` tokens), each wave taking 16-byte
-//            pieces of consecutive token rows), as the decode reads them.
+//            pieces of consecutive token rows), as the decode reads them;
+//            1, 2 or 4 token rows per thread in flight.
 // Loaded values are folded into one word per thread that is stored only if it
 // equals a value the data cannot produce, so no load can be dropped and
 // almost nothing is written.
@@ -60,8 +61,10 @@ struct PagedArgs {
 
 // One workgroup per (KV head g, sequence s, split j). Lanes of a wave cover
 // LPT = row_bytes / 16 consecutive 16-byte pieces of one token's row, so a
-// wave reads 64 / LPT consecutive tokens per load; the four waves interleave
-// by load. Tokens past the context or in an invalid block are skipped.
+// workgroup load covers 256 / LPT consecutive tokens; each thread issues the
+// K and V loads of U such tokens (U workgroup loads apart) before folding any.
+// Tokens past the context or in an invalid block are skipped.
+template <int U>
 __global__ void __launch_bounds__(kThreads) paged_probe_kernel(PagedArgs a) {
   const int g = blockIdx.x, s = blockIdx.y, j = blockIdx.z;
   int ctx = a.ctx_lens[s];
@@ -78,13 +81,25 @@ __global__ void __launch_bounds__(kThreads) paged_probe_kernel(PagedArgs a) {
   const int32_t* trow = a.tables + (size_t)s * a.max_blocks;
   const int bmask = (1 << a.block_shift) - 1;
   uint32_t acc = 0;
-  for (int t = t0 + threadIdx.x / lpt; t < t1; t += tpl) {
-    const int blk = trow[t >> a.block_shift];
-    if ((unsigned)blk >= (unsigned)a.num_blocks) continue;
-    const size_t off = (((size_t)blk << a.block_shift) + (size_t)(t & bmask)) * rsb + head_off;
-    const uint4 k = ld_nt(reinterpret_cast<const uint4*>(a.k_pool + off));
-    const uint4 v = ld_nt(reinterpret_cast<const uint4*>(a.v_pool + off));
-    acc ^= k.x ^ k.y ^ k.z ^ k.w ^ v.x ^ v.y ^ v.z ^ v.w;
+  for (int t = t0 + threadIdx.x / lpt; t < t1; t += tpl * U) {
+    uint4 k[U], v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int tt = t + u * tpl;
+      k[u] = v[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (tt < t1) {
+        const int blk = trow[tt >> a.block_shift];
+        if ((unsigned)blk < (unsigned)a.num_blocks) {
+          const size_t off = (((size_t)blk << a.block_shift) + (size_t)(tt & bmask)) * rsb +
+                             head_off;
+          k[u] = ld_nt(reinterpret_cast<const uint4*>(a.k_pool + off));
+          v[u] = ld_nt(reinterpret_cast<const uint4*>(a.v_pool + off));
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      acc ^= k[u].x ^ k[u].y ^ k[u].z ^ k[u].w ^ v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   sink_if_impossible(acc, a.sink);
 }
@@ -110,15 +125,18 @@ int pkv_probe_stream(const void* buf, size_t bytes, int32_t blocks, void* sink, 
 // through `tables` (the decode's pool layout [num_blocks, block_size,
 // num_kv_heads, row_bytes]). row_bytes: bytes of one KV head's row (a multiple
 // of 16, at most 1024); block_size a power of two; `sink` needs
-// num_kv_heads * num_seqs * ceil(max_ctx / partition) words.
+// num_kv_heads * num_seqs * ceil(max_ctx / partition) words; unroll: token
+// rows per thread in flight, 1, 2 or 4.
 int pkv_probe_paged(const void* k_pool, const void* v_pool, const int32_t* tables,
                     int32_t max_blocks, const int32_t* context_lens, int32_t num_seqs,
                     int32_t max_ctx, int32_t num_kv_heads, int32_t row_bytes, int32_t block_size,
-                    int32_t num_blocks, int32_t partition, void* sink, void* stream) {
+                    int32_t num_blocks, int32_t partition, int32_t unroll, void* sink,
+                    void* stream) {
   if (!k_pool || !v_pool || !tables || !context_lens || !sink || num_seqs < 1 ||
       num_seqs > 65535 || num_kv_heads < 1 || row_bytes < 16 || row_bytes % 16 ||
       row_bytes > 1024 || block_size < 1 || (block_size & (block_size - 1)) || partition < 1 ||
-      max_ctx < 1 || num_blocks < 1 || max_blocks < 1)
+      max_ctx < 1 || num_blocks < 1 || max_blocks < 1 ||
+      (unroll != 1 && unroll != 2 && unroll != 4))
     return 3;
   PagedArgs a;
   a.k_pool = static_cast<const char*>(k_pool);
@@ -135,8 +153,14 @@ int pkv_probe_paged(const void* k_pool, const void* v_pool, const int32_t* table
   a.num_blocks = num_blocks;
   const int splits = (max_ctx + partition - 1) / partition;
   if (splits > 65535) return 3;
-  hipLaunchKernelGGL(paged_probe_kernel, dim3(num_kv_heads, num_seqs, splits), dim3(kThreads), 0,
-                     reinterpret_cast<hipStream_t>(stream), a);
+  const dim3 grid(num_kv_heads, num_seqs, splits);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (unroll == 1)
+    hipLaunchKernelGGL(paged_probe_kernel<1>, grid, dim3(kThreads), 0, st, a);
+  else if (unroll == 2)
+    hipLaunchKernelGGL(paged_probe_kernel<2>, grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(paged_probe_kernel<4>, grid, dim3(kThreads), 0, st, a);
   return status(hipGetLastError());
 }
 
