@@ -147,8 +147,9 @@ pkv_status pkv_write(const void* k, const void* v, const int32_t* slot_mapping,
  * instead each KV head's sequences, laid end to end (each non-empty one
  * preceded by 128 tokens that stand for a piece's fixed cost), into one
  * range per workgroup, two workgroups per CU, each range at least the
- * automatic partition long; a workgroup runs the parts of every sequence its
- * range touches, one after another (pkv_decode_schedule tells which cut a
+ * automatic partition long (the half of the workgroups that reach their CU
+ * first take ranges 9/64 longer than the rest); a workgroup runs the parts
+ * of every sequence its range touches, one after another (pkv_decode_schedule tells which cut a
  * call uses). Each piece of
  * a sequence with more than one yields a partial (running max m in log2
  * units, exp-sum l, unnormalised o) in `workspace`;

@@ -29,8 +29,16 @@ constexpr int64_t kSchedMinPieceBytes = 128 << 10;   // K+V bytes of a piece wor
 // with the 128-token charge (64: 125.4, 256: 125.6, 512: 133.8); with equal
 // ranges, one workgroup per CU 175, 1.5: 156, 2.5: 152, 3: 144 us. Its TP=8
 // shard (86 MB, 1 KV head) stays on 256-token pieces: 30.2 against 39.6 us.
+// The first-dispatched half of a head's ranges is 9/64 longer than the mean:
+// the older of a CU's two workgroups streams faster, and with equal ranges it
+// ended ~15 us before the other (per-workgroup ends from the traced build).
+// Measured on the same step (7 and 9 interleaved rounds on two boxes): equal
+// ranges 124.5 / 123.4 us; 4/64: 122.8; 5/64: 121.8; 7/64: 120.4; 8/64:
+// 119.2 / 121.1; 9/64: 119.6; 10/64: 119.7 / 120.1; 12/64: 118.8 / 123.2 (the
+// spread grows); 16/64: 126.7; 20/64: 129.8.
 constexpr int kSkWgPerCu = 2;
 constexpr int kSkAlphaTokens = 128;
+constexpr int kSkFirstExtra64 = 9;
 constexpr int64_t kSkMinWgBytes = 1 << 20;
 // Merge counters: a fixed area at the start of every workspace, so that calls
 // of any size sharing one buffer never write partials where another counts.
@@ -84,6 +92,7 @@ struct DecodePlan {
   int sched_sk = 0;         // > 0: stream-K ranges, workgroups per KV head
   int sk_min_units = 0;
   int sk_alpha = 0;
+  int sk_first_extra = 0;
   int pair_rep = 0;         // > 0: KV heads read in pairs (real group size)
   pkv_pool_desc view{};     // the pool as the kernels read it
   size_t ws_ml_offset = 0;   // partial (m, l) pairs, after the counter area
@@ -235,7 +244,7 @@ pkv_status plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks
   // (a tile within one block), its rows are unpaired and of 256 bytes or more
   // (the compiled stream-K variants) and the ranges are long. The partition is the
   // least range (a bound on the partial slots a sequence can need).
-  plan->sched_sk = plan->sk_min_units = plan->sk_alpha = 0;
+  plan->sched_sk = plan->sk_min_units = plan->sk_alpha = plan->sk_first_extra = 0;
   const int A = plan->view.block_size;
   const int heads = plan->view.num_kv_heads;
   const int64_t wgs = (int64_t)kSkWgPerCu * num_cus();
@@ -252,6 +261,7 @@ pkv_status plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks
       plan->sched_sk = (int)(wgs / heads);
       plan->sk_min_units = mu;
       plan->sk_alpha = alpha;
+      plan->sk_first_extra = kSkFirstExtra64;
       plan->sched_q = 0;
       plan->sched_align = A;
       plan->splits = (int)J;
@@ -419,6 +429,7 @@ pkv_status decode_impl(Phase phase, const void* q, int32_t num_seqs, int32_t num
   a.sched_sk = plan.sched_sk;
   a.sk_min_units = plan.sk_min_units;
   a.sk_alpha = plan.sk_alpha;
+  a.sk_first_extra = plan.sk_first_extra;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.cu_q = nullptr;
   a.total_q = 0;

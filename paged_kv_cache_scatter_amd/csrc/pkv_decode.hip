@@ -1393,25 +1393,38 @@ decode_partials_kernel(DecodeArgs a) {
   if constexpr (!SK) {
     piece();
   } else {
-  // ---- stream-K: the pieces of workgroup i's range [i E, (i + 1) E) of the
-  // head's stream, in sequence order. E = ceil(U / sched_sk), at least
-  // sk_min_units; the range of the last workgroup with tokens runs to the end,
-  // so that empty sequences after the last token belong to it. A sequence's
-  // tokens occupy units [a0, a1); its piece in range i is partial slot
-  // i - floor(a0 / E) of floor((a1 - 1) / E) - floor(a0 / E) + 1. An empty
-  // sequence (a0 == a1) is one piece, of the range holding a0.
+  // ---- stream-K: the pieces of workgroup i's range [start(i), start(i + 1))
+  // of the head's stream of U units, in sequence order. The first H =
+  // sched_sk / 2 ranges are E1 = ceil(U (64 + sk_first_extra) / (64 sched_sk))
+  // units long, the others E2 = ceil((U - H E1) / (sched_sk - H)), both at
+  // least sk_min_units: the first half of a head's workgroups reaches each
+  // CU first, and the older workgroup of a CU streams faster (with equal
+  // ranges it ended ~15 us before the other, leaving its CU half occupied).
+  // The range of the last workgroup with tokens runs to the end, so that
+  // empty sequences after the last token belong to it. A sequence's tokens
+  // occupy units [a0, a1); its piece in range i is partial slot i - idx(a0)
+  // of idx(a1 - 1) - idx(a0) + 1, idx(u) being the range holding unit u. An
+  // empty sequence (a0 == a1) is one piece, of the range holding a0.
   if (!Lds<T, HD, REP>::uniform(bshift)) return;   // the planner never asks for it
   int* st_lds = reinterpret_cast<int*>(smem + round16(Lds<T, HD, REP>::bytes(0)));
   int* len_lds = st_lds + a.num_seqs;
   const int U = sk_layout(a, lim, st_lds, len_lds, len_lds + a.num_seqs);
   const int la = __builtin_ctz((unsigned)a.sched_align);
   const int i = blockIdx.y;
-  int E = (int)(((int64_t)U + a.sched_sk - 1) / a.sched_sk);
-  E = E < a.sk_min_units ? a.sk_min_units : E;
-  const int last_active = U > 0 ? (U - 1) / E : 0;
+  const int Nh = a.sched_sk, H = Nh / 2, mu = a.sk_min_units;
+  const int64_t e1 = ((int64_t)U * (64 + a.sk_first_extra) + 64ll * Nh - 1) / (64ll * Nh);
+  const int E1 = (int)(e1 < mu ? mu : e1);
+  const int64_t HE = (int64_t)H * E1, rest = (int64_t)U - HE;
+  const int64_t e2 = Nh == H ? E1 : rest > 0 ? (rest + (Nh - H) - 1) / (Nh - H) : mu;
+  const int E2 = (int)(e2 < mu ? mu : e2);
+  auto start = [&](int k) -> int64_t {
+    return k <= H ? (int64_t)k * E1 : HE + (int64_t)(k - H) * E2;
+  };
+  auto idx = [&](int u) -> int { return u < HE ? u / E1 : H + (int)((u - HE) / E2); };
+  const int last_active = U > 0 ? idx(U - 1) : 0;
   if (i > last_active) return;
-  const int lo = i * E;
-  const int64_t hi = i == last_active ? INT64_MAX : (int64_t)(i + 1) * E;
+  const int lo = (int)start(i);
+  const int64_t hi = i == last_active ? INT64_MAX : start(i + 1);
   auto units = [&](int sq) { return (len_lds[sq] + a.sched_align - 1) >> la; };
   // first sequence with tokens past lo, or empty at or after it
   int l = 0, r = a.num_seqs;
@@ -1436,8 +1449,8 @@ decode_partials_kernel(DecodeArgs a) {
       const int e1 = (b1 - a0) << la;
       p.t0 = (b0 - a0) << la;
       p.t1 = e1 < c ? e1 : c;
-      p.slot = i - a0 / E;
-      p.n = (a1 - 1) / E - a0 / E + 1;
+      p.slot = i - idx(a0);
+      p.n = idx(a1 - 1) - idx(a0) + 1;
     }
     // memory safety whatever the layout gave: an inconsistent piece does no work
     if (p.t0 < 0 || p.t0 > p.t1 || p.t1 > p.ctx || p.ctx > lim || p.slot < 0 ||

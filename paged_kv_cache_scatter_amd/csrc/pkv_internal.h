@@ -116,13 +116,16 @@ struct DecodeArgs {
   // kSchedMaxSeqs sequences): each KV head's sequences are laid end to end
   // as one stream of sched_align-token units, every non-empty sequence
   // preceded by sk_alpha units that stand for the fixed cost of a piece
-  // (they hold no tokens). The stream is cut into sched_sk equal ranges of
-  // at least sk_min_units units; workgroup i of a head runs, one after
-  // another, the pieces of every sequence its range touches. Piece k of a
-  // sequence is its part in the k-th range it touches (its partial slot k).
+  // (they hold no tokens). The stream is cut into sched_sk ranges of at
+  // least sk_min_units units, the first half of them sk_first_extra / 64
+  // longer than the mean and the rest sharing what is left; workgroup i of
+  // a head runs, one after another, the pieces of every sequence its range
+  // touches. Piece k of a sequence is its part in the k-th range it touches
+  // (its partial slot k).
   int32_t sched_sk;
   int32_t sk_min_units;
   int32_t sk_alpha;
+  int32_t sk_first_extra;
   // Paired KV heads (> 0: the group size of the real heads): the pool is read
   // as num_kv_heads virtual heads of two adjacent real heads each (rows of
   // 2 * head_dim, the same bytes), a workgroup serving both groups' query
