@@ -297,24 +297,34 @@ __device__ __forceinline__ void attend_rows(const PrefillArgs& a, const Work& wk
       }
     }
 
-    // online softmax per row; p overwrites the scores
-    const bool masked = any_bad || __any(k0 + KT > rmin);
+    // online softmax per row; p overwrites the scores. The mask test is
+    // uniform over the tile: only the tiles that reach past a row's last
+    // visible key (or hold an invalid block) run the masking pass. (Tested
+    // inside the per-score loop it became a branch per score: 3.03 against
+    // 2.93 ms for the LLaMA-2-70B layer's chunked prefill.)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int nb = 0; nb < NBLK; ++nb) sc[kb][nb] *= a.scale_log2;
+    if (any_bad || __any(k0 + KT > rmin)) {
+#pragma unroll
+      for (int nb = 0; nb < NBLK; ++nb)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = k0 + kb * 16 + grp * 4 + i;
+            const bool vis = key < rhi[nb] && (!any_bad || tbl[(key >> bshift) - tb0] >= 0);
+            sc[kb][nb][i] = vis ? sc[kb][nb][i] : -INFINITY;
+          }
+    }
 #pragma unroll
     for (int nb = 0; nb < NBLK; ++nb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = sc[kb][nb][i] * a.scale_log2;
-          if (masked) {
-            const int key = k0 + kb * 16 + grp * 4 + i;
-            const bool vis = key < rhi[nb] && (!any_bad || tbl[(key >> bshift) - tb0] >= 0);
-            v = vis ? v : -INFINITY;
-          }
-          sc[kb][nb][i] = v;
-          mx = fmaxf(mx, v);
-        }
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[kb][nb][i]);
       // the row's 16 lanes of each of the four lane groups: join the groups
       // with VALU cross-lane swaps (lanes i ^ 16, then i ^ 32)
       mx = join16<true>(mx);
