@@ -23,12 +23,17 @@ constexpr int kMaxSplits = 4096;      // splits per sequence (bounds the merge k
 constexpr int64_t kSchedMinPieceBytes = 128 << 10;   // K+V bytes of a piece worth a lookup
 // Stream-K ranges (DecodeArgs::sched_sk): two workgroups per CU, so that
 // every CU holds two equal ranges; a piece is charged 128 tokens of cost;
-// used when, at the largest contexts, a range would average at least 1 MiB of
-// K/V. Measured on the LLaMA-2-70B layer step (A/B on one box, 5 interleaved
+// used when, at the largest contexts, a range would average at least 256 KiB
+// of K/V. Measured on the LLaMA-2-70B layer step (A/B on one box, 5 interleaved
 // rounds): 134.5 us with the piece schedule, 128.3 with equal ranges, 124.5
 // with the 128-token charge (64: 125.4, 256: 125.6, 512: 133.8); with equal
 // ranges, one workgroup per CU 175, 1.5: 156, 2.5: 152, 3: 144 us. Its TP=8
-// shard (86 MB, 1 KV head) stays on 256-token pieces: 30.2 against 39.6 us.
+// shard (86 MB, 1 KV head): 28.6 us against 30.5 with 256-token pieces.
+// Head_dim 128, 8 query heads per KV head, log-uniform contexts up to 8,192,
+// block tables rotated past the last-level cache (ranges / pieces, us): at
+// 64 MiB of K/V at the largest contexts, 22.6 / 21.4; at 128 MiB, 25.5 / 25.3,
+// 25.3 / 23.8, 23.7 / 23.7 and, at a uniform 4,096, 33.8 / 40.4; at 256 MiB,
+// 29.3 / 31.4 and 33.5 / 39.3; at 384-512 MiB, 6.3-8.1 us less.
 // The first-dispatched half of a head's ranges is 9/64 longer than the mean:
 // the older of a CU's two workgroups streams faster, and with equal ranges it
 // ended ~15 us before the other (per-workgroup ends from the traced build).
@@ -39,7 +44,7 @@ constexpr int64_t kSchedMinPieceBytes = 128 << 10;   // K+V bytes of a piece wor
 constexpr int kSkWgPerCu = 2;
 constexpr int kSkAlphaTokens = 128;
 constexpr int kSkFirstExtra64 = 9;
-constexpr int64_t kSkMinWgBytes = 1 << 20;
+constexpr int64_t kSkMinWgBytes = 1 << 18;
 // Merge counters: a fixed area at the start of every workspace, so that calls
 // of any size sharing one buffer never write partials where another counts.
 // Launches with more (sequence, KV head) pairs merge in a second kernel.

@@ -224,8 +224,10 @@ def test_piece_schedule_needs_large_pieces(lib):
 def test_decode_schedule_choice(lib):
     """pkv_decode_schedule: with partition 0, the 70B layer shape (64
     sequences, 8 KV heads of 128 bf16 dims, contexts up to 8192) takes the
-    stream-K ranges; its explicit automatic partition, its TP=8 shard (one KV
-    head: ranges of under 1 MiB of K/V at the largest contexts), 192
+    stream-K ranges, and so does its TP=8 shard (one KV head: 256 MiB of K/V
+    at the largest contexts, 512 KiB per range of 512); 32 of the shard's
+    sequences sit on the 256 KiB bound (8192: ranges, 8191: pieces). The
+    explicit automatic partition, 192
     Llama-3.2-1B sequences (one piece each, longest first) and 8 x 2048 (the
     plain grid) do not. The workspace size covers both cuts."""
     d70 = _desc(nb=32769, bs=16, hkv=8, hd=128)
@@ -239,7 +241,9 @@ def test_decode_schedule_choice(lib):
     assert lib.pkv_decode_workspace_bytes(64, 64, 8192, 0, ctypes.byref(d70)) == \
         COUNTER_AREA + rows * 2 * 4 + rows * 128 * 4
     shard = _desc(nb=32769, bs=16, hkv=1, hd=128)
-    assert sched(64, 8, 8192, 0, ctypes.byref(shard)) == 1
+    assert sched(64, 8, 8192, 0, ctypes.byref(shard)) == 3
+    assert sched(32, 8, 8192, 0, ctypes.byref(shard)) == 3
+    assert sched(32, 8, 8191, 0, ctypes.byref(shard)) == 1
     d1b = _desc(nb=32768, bs=16, hkv=8, hd=64)
     assert sched(192, 32, 2048, 0, ctypes.byref(d1b)) == 2
     assert sched(8, 32, 2048, 0, ctypes.byref(d1b)) == 0
