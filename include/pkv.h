@@ -140,10 +140,13 @@ pkv_status pkv_write(const void* k, const void* v, const int32_t* slot_mapping,
  * piece, a longer one becomes one tail piece of its own (shorter than a
  * partition); the launch runs all full pieces first, then
  * the tail pieces, longer ones first (near-equal pieces keep every workgroup
- * stream of the GPU equally loaded and the last pieces short). With
+ * stream of the GPU equally loaded and the last pieces short). When every
+ * context fits one piece, the sequences run longest first (32 length
+ * classes), their ranks dealt over the passes in which the CUs take the grid
+ * so that the lengths each CU serves add up to near the mean. With
  * partition 0, when a tile lies within one block and the contexts are long
  * (num_seqs * num_kv_heads * max_context_len rows of K and V average at least
- * 1 MiB over two workgroups per CU), pkv_decode and pkv_decode_step cut
+ * 256 KiB over two workgroups per CU), pkv_decode and pkv_decode_step cut
  * instead each KV head's sequences, laid end to end (each non-empty one
  * preceded by 128 tokens that stand for a piece's fixed cost), into one
  * range per workgroup, two workgroups per CU, each range at least the

@@ -911,16 +911,41 @@ __device__ __forceinline__ bool find_piece(const DecodeArgs& a, int pid, int lim
   return pc.s >= 0;
 }
 
+// Rank (longest first) of the sequence that grid index `pid` runs, when the
+// CUs take the grid in passes of n sequences, position k of every pass on
+// the same CUs. The aim is an equal sum of lengths per position. Pairs of
+// full passes run the second reversed (rank k with rank n - 1 - k). An odd
+// count of full passes ends with three passes dealt as k, (k + n/2) mod n and
+// n - 1 - (2 (k mod n/2) + [k >= n/2]) (n even), whose position sums differ
+// by at most one rank step; a partial last pass keeps its order.
+__device__ __forceinline__ int lpt_rank(int pid, int n, int num_seqs) {
+  const int full = num_seqs / n;
+  const int ps = pid / n, k = pid - ps * n;
+  if (ps >= full) return pid;
+  int off;
+  if ((full & 1) && full >= 3 && ps >= full - 3 && (n & 1) == 0) {
+    const int q = ps - (full - 3), h = n >> 1;
+    off = q == 0 ? k : q == 1 ? (k + h) % n : n - 1 - (2 * (k % h) + (k >= h));
+  } else {
+    off = (ps & 1) ? n - 1 - k : k;
+  }
+  return ps * n + off;
+}
+
 // Sequence number `pid` in longest-first order (see DecodeArgs::sched_lpt):
 // every thread classifies four consecutive sequences by length (class
-// floor(kLenClasses * L / (lim + 1)), longest class first), a workgroup scan
-// of the class counts gives each thread its offsets, and the thread holding
-// the sequence publishes it as a one-piece Piece. Returns false (uniformly)
-// when pid is past the last sequence.
+// floor(kLenClasses * L / (lim + 1)), longest class first) and counts them
+// into an LDS histogram; the rank's class and its place within the class
+// follow from the counts, and a workgroup scan of the thread's own members of
+// that class finds the sequence (index order within a class), which the
+// thread holding it publishes as a one-piece Piece. With lpt_pass > 0 the
+// ranks are dealt in passes of lpt_pass, every second pass reversed, so that
+// the CUs that take the longest of one pass take the shortest of the next.
+// Returns false (uniformly) when pid is past the last sequence.
 __device__ __forceinline__ bool find_sequence_lpt(const DecodeArgs& a, int pid, int lim,
                                                   Piece& pc, int* lds) {
-  static_assert(kLenClasses == 4, "two 16-bit class counts per scanned word");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int* hist = lds + 32;   // kLenClasses counts
   const float cls_scale = (float)kLenClasses / (float)(lim + 1);
   int L[4], cls[4];
 #pragma unroll
@@ -928,63 +953,51 @@ __device__ __forceinline__ bool find_sequence_lpt(const DecodeArgs& a, int pid, 
     const int sq = tid * 4 + i;
     L[i] = sq < a.num_seqs ? a.ctx_lens[sq] : 0;
   }
-  uint32_t hi = 0, lo = 0;   // counts of segments 0, 1 (hi) and 2, 3 (lo), 16 bits each
+  for (int c = tid; c < kLenClasses; c += kThreads) hist[c] = 0;
+  if (tid == 0) lds[16] = -1;
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int sq = tid * 4 + i;
     L[i] = L[i] < 0 ? 0 : (L[i] > lim ? lim : L[i]);
     int c = (int)((float)L[i] * cls_scale);
     c = c > kLenClasses - 1 ? kLenClasses - 1 : c;
-    const int seg = kLenClasses - 1 - c;   // longest class is segment 0
-    cls[i] = sq < a.num_seqs ? seg : -1;
-    if (cls[i] >= 0) {
-      if (seg < 2) hi += 1u << (16 * (1 - seg));
-      else lo += 1u << (16 * (3 - seg));
-    }
+    cls[i] = sq < a.num_seqs ? kLenClasses - 1 - c : -1;   // longest class first
+    if (cls[i] >= 0) atomicAdd(&hist[cls[i]], 1);
   }
-  const uint32_t ih = wave_incl_scan(hi), il = wave_incl_scan(lo);
-  if (lane == 63) {
-    lds[w] = (int)ih;
-    lds[4 + w] = (int)il;
-  }
-  lds[16] = -1;
   __syncthreads();
-  uint32_t ph = 0, pl = 0, th = 0, tl = 0;
-#pragma unroll
-  for (int k = 0; k < kWaves; ++k) {
-    const uint32_t vh = (uint32_t)lds[k], vl = (uint32_t)lds[4 + k];
-    if (k < w) {
-      ph += vh;
-      pl += vl;
-    }
-    th += vh;
-    tl += vl;
+  if (pid >= a.num_seqs) return false;
+  int r = pid;
+  if (a.lpt_pass > 0) r = lpt_rank(pid, a.lpt_pass, a.num_seqs);
+  int seg = 0, base = 0;   // the class holding rank r, and its first rank
+  for (; seg < kLenClasses - 1; ++seg) {
+    const int h = hist[seg];
+    if (r < base + h) break;
+    base += h;
   }
-  const uint32_t eh = ph + ih - hi, el = pl + il - lo;   // exclusive, this thread
-  const uint32_t tot[4] = {th >> 16, th & 0xFFFF, tl >> 16, tl & 0xFFFF};
-  const uint32_t exc[4] = {eh >> 16, eh & 0xFFFF, el >> 16, el & 0xFFFF};
-  const uint32_t mine[4] = {hi >> 16, hi & 0xFFFF, lo >> 16, lo & 0xFFFF};
-  uint32_t u = (uint32_t)pid;
-  int seg = 0;
+  const uint32_t k = (uint32_t)(r - base);   // place within the class
+  uint32_t mine = 0;
 #pragma unroll
-  for (int c = 0; c < kLenClasses - 1; ++c) {
-    if (seg == c && u >= tot[c]) {
-      u -= tot[c];
-      seg = c + 1;
-    }
-  }
-  if (u >= tot[seg]) return false;
-  uint32_t k = u - exc[seg];
-  if (k < mine[seg]) {
+  for (int i = 0; i < 4; ++i) mine += cls[i] == seg;
+  const uint32_t incl = wave_incl_scan(mine);
+  if (lane == 63) lds[w] = (int)incl;
+  __syncthreads();
+  uint32_t pre = 0;
+#pragma unroll
+  for (int q = 0; q < kWaves; ++q)
+    if (q < w) pre += (uint32_t)lds[q];
+  const uint32_t exc = pre + incl - mine;
+  if (k >= exc && k < exc + mine) {
+    uint32_t kk = k - exc;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (cls[i] == seg) {
-        if (k == 0) {
+        if (kk == 0) {
           lds[16] = tid * 4 + i;
           lds[17] = L[i];
           break;
         }
-        --k;
+        --kk;
       }
     }
   }

@@ -110,7 +110,10 @@ struct DecodeArgs {
   // Longest-first order for single-piece plans (at most kSchedMaxSeqs
   // sequences): the grid's (y, z) plane enumerates the sequences by length
   // class, longest class first (kLenClasses classes of the length range).
+  // lpt_pass > 0: ranks are dealt in passes of lpt_pass sequences (the
+  // workgroups one round of the CUs takes), every second pass reversed.
   int32_t sched_lpt;
+  int32_t lpt_pass;
   // Stream-K ranges (sched_sk > 0: workgroups per KV head; no shared prefix,
   // no prefill rows, in-launch merge, a uniform-id kernel, at most
   // kSchedMaxSeqs sequences): each KV head's sequences are laid end to end
@@ -133,7 +136,7 @@ struct DecodeArgs {
   // only; q and out keep the real head_dim, the workspace the virtual one.
   int32_t pair_rep;
 };
-constexpr int kLenClasses = 4;
+constexpr int kLenClasses = 32;
 constexpr int kSchedMaxSeqs = 1024;   // 4 sequences per thread of the scan
 
 // Pieces of a context of L tokens under the piece schedule (P large, Q small
