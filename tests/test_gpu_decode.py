@@ -57,6 +57,37 @@ def test_tp8_shard_of_the_70b_layer_every_sequence():
     note(f"{pc.wl.name}: all {pc.wl.num_seqs} sequences, max error {err:.3e}")
 
 
+@pytest.mark.parametrize("hd,hq,S", [(128, 64, 128), (128, 64, 167), (128, 64, 300),
+                                     (64, 32, 200)])
+def test_longest_first_dealt_over_cu_passes(hd, hq, S):
+    """One piece per sequence, longest first, the ranks dealt over the passes
+    in which the CUs take the grid (one workgroup per CU: 32 sequences at 8
+    KV heads of 128 dims, 64 at head_dim 64 read as 4 paired heads). Four full
+    passes (reversed pairs); five and a partial one (a reversed pair, then the
+    three-pass deal); nine and a partial one; paired heads with three full
+    passes and a partial one. Each sequence must run exactly once: the output
+    starts as NaN, so a rank map that is not a permutation leaves rows NaN."""
+    rng = np.random.default_rng(7000 + S)
+    bs = 16
+    ctx = rng.integers(64, 2049, S).astype(np.int32)
+    ctx[rng.integers(0, S)] = 2048
+    nb = -(-ctx // bs)
+    perm = rng.permutation(int(nb.sum())) + 1
+    tables, k = [], 0
+    for n in nb:
+        tables.append(list(perm[k:k + n]))
+        k += int(n)
+    wl = make_custom(tables, ctx, dtype="bf16", num_q_heads=hq, num_kv_heads=8, head_dim=hd,
+                     block_size=bs, num_blocks=int(nb.sum()) + 1, seed=S,
+                     name=f"longest-first hd{hd} {S} seqs")
+    pc = PoolCase(wl)
+    assert pkv.decode_schedule(S, hq, int(ctx.max()), pc.k_pool) == "longest_first"
+    out = torch.full(wl.q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    got = out_f64(pc.decode(out=out), "bf16")
+    err = check_close(got, pc.ref_decode(), "bf16", wl.name)
+    note(f"{wl.name}: all sequences, max error {err:.3e}")
+
+
 @pytest.mark.parametrize("cfg,S,parts", [(2, None, [64, 128, 256]),
                                          (3, None, [256, 512, 2048]),
                                          (5, 6, [256, 1024, 4096, 8192])])
