@@ -331,7 +331,11 @@ pkv_status pkv_decode_step_noalloc(const void* q, const void* k_new, const void*
  *   prefix_lens[i] (and <= max_context_len); max_tail_len >= ctx_s - min(ctx_s,
  *   P_i) for every s, or < 0 for max_context_len (positions past that bound
  *   are not attended). partition: tokens per tail split (0 = auto from
- *   max_tail_len), as in pkv_decode.
+ *   max_tail_len), as in pkv_decode. With partition 0 and tails long enough
+ *   (the stream-K rule of pkv_decode with max_tail_len as the longest
+ *   context), the tails are laid end to end per KV head and cut into
+ *   stream-K ranges as in pkv_decode, each non-empty tail charged 256
+ *   tokens; otherwise each tail is cut into splits of `partition` tokens.
  * workspace: pkv_decode_shared_workspace_bytes(...) bytes (device, 16-byte
  *   aligned); 0 when no shared pass and no split is needed. Its counter
  *   area (the first 256 KiB) must be zero before the first call, as for

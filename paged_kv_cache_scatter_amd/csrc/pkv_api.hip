@@ -49,6 +49,12 @@ constexpr bool kLptDealPasses = true;
 // spread grows); 16/64: 126.7; 20/64: 129.8.
 constexpr int kSkWgPerCu = 2;
 constexpr int kSkAlphaTokens = 128;
+// Shared-prefix tails on stream-K ranges: each tail piece also merges the
+// shared pass's partials (16 on the LLaMA-2-70B layer with a 4096-token
+// prompt, 64 users): a charge of 256 tokens per tail. Measured on that case
+// (3 rounds on one box, the whole call with its shared pass): 128 tokens
+// 148.7-148.9 us, 256: 144.4-144.9, 512: 148.3-148.5.
+constexpr int kSkTailAlphaTokens = 256;
 constexpr int kSkFirstExtra64 = 9;
 constexpr int64_t kSkMinWgBytes = 1 << 18;
 // Merge counters: a fixed area at the start of every workspace, so that calls
@@ -319,7 +325,8 @@ int64_t shared_min_saved_bytes() {
 // compile); the plan is then plain decode.
 pkv_status plan_shared(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
                        int32_t max_ctx, const SharedIn& in, int32_t partition,
-                       const pkv_pool_desc* pool, DecodePlan* plan, SharedDesc* sd) {
+                       const pkv_pool_desc* pool, DecodePlan* plan, SharedDesc* sd,
+                       bool allow_sk = true) {
   *sd = SharedDesc{};
   pkv_status st = plan_decode(num_seqs, num_q_heads, max_blocks, max_ctx, partition, pool, plan);
   if (st != PKV_OK) return st;
@@ -341,9 +348,16 @@ pkv_status plan_shared(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks
   const int64_t saved = (int64_t)(num_seqs - in.num_groups) * in.max_prefix * 2 *
                         pool->num_kv_heads * pool->head_dim * dtype_bytes(pool->dtype);
   if (saved < shared_min_saved_bytes()) return PKV_OK;
+  // The tails: stream-K ranges over the laid-end-to-end tails when they are
+  // long enough (the only schedule that knows tails), else the plain grid.
   const int tail = in.max_tail < 0 ? max_ctx : in.max_tail;
-  st = plan_decode(num_seqs, num_q_heads, max_blocks, tail, partition, pool, plan, false, false);
+  st = plan_decode(num_seqs, num_q_heads, max_blocks, tail, partition, pool, plan, true, false,
+                   allow_sk);
+  if (st == PKV_OK && plan->sched_sk == 0)
+    st = plan_decode(num_seqs, num_q_heads, max_blocks, tail, partition, pool, plan, false, false);
   if (st != PKV_OK) return st;
+  // a tail's piece also merges the shared pass's partials: a larger charge
+  if (plan->sched_sk > 0) plan->sk_alpha = std::max(1, kSkTailAlphaTokens / plan->sched_align);
   const int64_t align = std::max(kSharedAlign, bs);
   const int64_t row_tiles = ((int64_t)in.max_group * plan->rep + kSharedRows - 1) / kSharedRows;
   const int64_t base = (int64_t)in.num_groups * pool->num_kv_heads * row_tiles;

@@ -802,6 +802,7 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
 // A workgroup's piece under the piece schedule.
 struct Piece {
   int s, t0, t1, slot, n, ctx;
+  int start;   // first token of a shared-prefix tail (0 without sharing)
 };
 
 // Piece number `pid` of the schedule (see DecodeArgs::sched_q): every thread
@@ -1014,22 +1015,48 @@ __device__ __forceinline__ bool find_sequence_lpt(const DecodeArgs& a, int pid, 
 // thread takes four consecutive sequences, a workgroup scan of their unit
 // counts (a non-empty sequence costs sk_alpha + ceil(L / A) units) gives
 // st[s], the unit where sequence s's tokens start, and len[s], its clamped
-// length. Returns the stream's total units. `tmp` holds kWaves ints; the
-// caller's later reads of st and len follow the barrier at the end.
+// length. With shared-prefix groups (a.sh.group_start) L is the tail past
+// the group's shared tokens, which start in `first` gets (the same group
+// and shared length as group_of and shared_len give, from the group table
+// staged in `gtab`, 2 * num_seqs ints). Returns the stream's total units.
+// `tmp` holds kWaves ints; the caller's later reads of st, len and first
+// follow the barrier at the end.
 __device__ __forceinline__ int sk_layout(const DecodeArgs& a, int lim, int* st, int* len,
-                                         int* tmp) {
+                                         int* tmp, int* first, int* gtab) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int la = __builtin_ctz((unsigned)a.sched_align);
-  int L[4];
+  const bool shared = a.sh.group_start != nullptr;
+  int L[4], F[4] = {0, 0, 0, 0};
   uint32_t u[4], sum = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {   // all four loads in flight together
     const int sq = tid * 4 + i;
     L[i] = sq < a.num_seqs ? a.ctx_lens[sq] : 0;
   }
+  if (shared) {
+    const int G = a.sh.num_groups;   // at most num_seqs (checked by the planner)
+    for (int k = tid; k < G; k += kThreads) {
+      gtab[k] = a.sh.group_start[k];
+      gtab[a.num_seqs + k] = shared_len(a.sh, k, lim, a.block_shift);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sq = tid * 4 + i;
+      int lo = 0, hi = G;   // the last group starting at or before sq (0 if none)
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (gtab[mid] <= sq) lo = mid;
+        else hi = mid;
+      }
+      const int c = L[i] < 0 ? 0 : (L[i] > lim ? lim : L[i]);
+      F[i] = G > 0 ? min(c, gtab[a.num_seqs + lo]) : 0;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     L[i] = L[i] < 0 ? 0 : (L[i] > lim ? lim : L[i]);
+    L[i] -= F[i];
     u[i] = ((uint32_t)L[i] + (uint32_t)a.sched_align - 1u) >> la;
     sum += u[i] ? u[i] + (uint32_t)a.sk_alpha : 0u;
   }
@@ -1051,6 +1078,7 @@ __device__ __forceinline__ int sk_layout(const DecodeArgs& a, int lim, int* st, 
     if (sq < a.num_seqs) {
       st[sq] = (int)(at + pad);
       len[sq] = L[i];
+      if (shared) first[sq] = F[i];
     }
     at += u[i] + pad;
   }
@@ -1135,6 +1163,12 @@ decode_partials_kernel(DecodeArgs a) {
   int nsplit;
   if (sched) {
     nsplit = pc.n;
+    if (SK && a.sh.group_start) {
+      // a shared-prefix tail: the shared pass's partials lead
+      start = pc.start;
+      nps = (start + a.sh.prefix_part - 1) / a.sh.prefix_part;
+      slot0 = a.sh.prefix_slots;
+    }
   } else if (a.sh.group_start) {
     start = min(ctx, shared_len(a.sh, group_of(a.sh, s), lim, bshift));
     nps = (start + a.sh.prefix_part - 1) / a.sh.prefix_part;
@@ -1147,7 +1181,7 @@ decode_partials_kernel(DecodeArgs a) {
   T* out = reinterpret_cast<T*>(a.out) + ((size_t)qrow * a.num_q_heads + hq0) * QHD;
 
   PKV_PHASE(1);
-  if (sched ? ctx == 0 : j >= nsplit) {
+  if (sched ? ctx == start : j >= nsplit) {
     if (j == 0 && nps == 0) {  // empty sequence: zeros
       for (int i = tid; i < REP * QHD; i += kThreads) out[i] = from_f32<T>(0.f);
     } else if (j == 0 && a.counters) {
@@ -1421,7 +1455,10 @@ decode_partials_kernel(DecodeArgs a) {
   if (!Lds<T, HD, REP>::uniform(bshift)) return;   // the planner never asks for it
   int* st_lds = reinterpret_cast<int*>(smem + round16(Lds<T, HD, REP>::bytes(0)));
   int* len_lds = st_lds + a.num_seqs;
-  const int U = sk_layout(a, lim, st_lds, len_lds, len_lds + a.num_seqs);
+  int* first_lds = len_lds + a.num_seqs + kWaves;   // shared-prefix tails only
+  const bool tails = a.sh.group_start != nullptr;
+  const int U = sk_layout(a, lim, st_lds, len_lds, len_lds + a.num_seqs, first_lds,
+                          first_lds + a.num_seqs);
   const int la = __builtin_ctz((unsigned)a.sched_align);
   const int i = blockIdx.y;
   const int Nh = a.sched_sk, H = Nh / 2, mu = a.sk_min_units;
@@ -1447,27 +1484,31 @@ decode_partials_kernel(DecodeArgs a) {
     else l = m + 1;
   }
   for (int sq = l; sq < a.num_seqs; ++sq) {
+    // c: the tokens of the stream (a tail with sharing), from token f on
     const int a0 = st_lds[sq], a1 = a0 + units(sq), c = len_lds[sq];
     if ((int64_t)a0 >= hi) break;
+    const int f = tails ? first_lds[sq] : 0;
     Piece p;
     p.s = sq;
-    p.ctx = c;
+    p.start = f;
+    p.ctx = f + c;
     if (a1 == a0) {
-      p.t0 = p.t1 = 0;
+      p.t0 = p.t1 = f;
       p.slot = 0;
       p.n = 1;
     } else {
       const int b0 = a0 > lo ? a0 : lo;
       const int b1 = (int64_t)a1 < hi ? a1 : (int)hi;
       const int e1 = (b1 - a0) << la;
-      p.t0 = (b0 - a0) << la;
-      p.t1 = e1 < c ? e1 : c;
+      p.t0 = f + ((b0 - a0) << la);
+      p.t1 = f + (e1 < c ? e1 : c);
       p.slot = i - idx(a0);
       p.n = idx(a1 - 1) - idx(a0) + 1;
     }
     // memory safety whatever the layout gave: an inconsistent piece does no work
-    if (p.t0 < 0 || p.t0 > p.t1 || p.t1 > p.ctx || p.ctx > lim || p.slot < 0 ||
-        p.slot >= p.n || p.n > a.num_splits)
+    if (p.start < 0 || p.t0 < p.start || p.t0 > p.t1 || p.t1 > p.ctx || p.ctx > lim ||
+        p.slot < 0 || p.slot >= p.n ||
+        p.n > a.num_splits - (tails ? a.sh.prefix_slots : 0))
       continue;
     __syncthreads();   // the previous piece is done with LDS
     s = qrow = p.s;
@@ -1544,7 +1585,9 @@ pkv_status launch_split(const DecodeArgs& a, hipStream_t st) {
   if (a.sched_sk > 0) {
     // stream-K: sched_sk ranges per KV head; the layout (start, length per
     // sequence, the scan's words) after the piece's LDS
-    lds = round16(L::bytes(0)) + (2 * a.num_seqs + kWaves) * (int)sizeof(int);
+    // (and, for shared-prefix tails, the tails' first tokens and the group table)
+    lds = round16(L::bytes(0)) +
+          ((a.sh.group_start ? 5 : 2) * a.num_seqs + kWaves) * (int)sizeof(int);
     grid = dim3(a.num_kv_heads, a.sched_sk, 1);
   } else if (a.sched_q > 0 || a.sched_lpt) {
     // pieces: at most num_splits per sequence (one in longest-first order)

@@ -221,6 +221,31 @@ def test_70b_layer_64_users_of_one_prompt():
     note(f"{wl.name}: all 64 sequences, max error {err:.3e}")
 
 
+@pytest.mark.parametrize("hkv,hq", [(1, 8), (8, 64)])
+def test_stream_k_tails(hkv, hq):
+    """Tails long enough for stream-K ranges (at least 256 KiB of K/V per range
+    at the longest tail): three groups with prompts of 1024, 2048 and 512
+    tokens; members of length 0, members whose context is exactly the prompt
+    (empty tail: only the shared pass's partials) or inside it, and tails up
+    to 6000 tokens laid end to end. Every sequence against the oracle."""
+    wl = make_shared([20, 30, 14], [1024, 2048, 512], ("uniform", 1, 6000), dtype=BF16,
+                     num_q_heads=hq, num_kv_heads=hkv, head_dim=128, seed=41 + hkv,
+                     name=f"stream-k tails hkv{hkv}")
+    wl.context_lens[1] = 0
+    wl.context_lens[2] = 1024
+    wl.context_lens[25] = 2048
+    wl.context_lens[26] = 700
+    wl.context_lens[60] = 512
+    pc = PoolCase(wl)
+    gs, pl = _groups(wl)
+    mt = _max_tail(wl, pl, gs)
+    assert pkv.decode_schedule(wl.num_seqs, hq, mt, pc.k_pool) == "stream_k"
+    got = out_f64(_shared(pc, gs, pl, max_tail=mt), wl.dtype)
+    assert not got[1].any()
+    err = check_close(got, pc.ref_decode(), wl.dtype, wl.name)
+    note(f"{wl.name}: all {wl.num_seqs} sequences, max error {err:.3e}")
+
+
 def test_default_rule_runs_plain_decode_at_the_pages_scale(monkeypatch):
     """With the default bound, 30 users of a 496-token shared prompt at the
     SmolLM2-135M shape (at most 22 MB of reads saved) run plain decode: the
