@@ -1021,11 +1021,12 @@ __device__ __forceinline__ bool find_sequence_lpt(const DecodeArgs& a, int pid, 
 // staged in `gtab`, 2 * num_seqs ints). Returns the stream's total units.
 // `tmp` holds kWaves ints; the caller's later reads of st, len and first
 // follow the barrier at the end.
+template <bool TAILS>
 __device__ __forceinline__ int sk_layout(const DecodeArgs& a, int lim, int* st, int* len,
                                          int* tmp, int* first, int* gtab) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int la = __builtin_ctz((unsigned)a.sched_align);
-  const bool shared = a.sh.group_start != nullptr;
+  constexpr bool shared = TAILS;
   int L[4], F[4] = {0, 0, 0, 0};
   uint32_t u[4], sum = 0;
 #pragma unroll
@@ -1033,7 +1034,7 @@ __device__ __forceinline__ int sk_layout(const DecodeArgs& a, int lim, int* st, 
     const int sq = tid * 4 + i;
     L[i] = sq < a.num_seqs ? a.ctx_lens[sq] : 0;
   }
-  if (shared) {
+  if constexpr (shared) {
     const int G = a.sh.num_groups;   // at most num_seqs (checked by the planner)
     for (int k = tid; k < G; k += kThreads) {
       gtab[k] = a.sh.group_start[k];
@@ -1078,7 +1079,7 @@ __device__ __forceinline__ int sk_layout(const DecodeArgs& a, int lim, int* st, 
     if (sq < a.num_seqs) {
       st[sq] = (int)(at + pad);
       len[sq] = L[i];
-      if (shared) first[sq] = F[i];
+      if constexpr (shared) first[sq] = F[i];
     }
     at += u[i] + pad;
   }
@@ -1087,10 +1088,13 @@ __device__ __forceinline__ int sk_layout(const DecodeArgs& a, int lim, int* st, 
 }
 
 // SK: the stream-K variant (DecodeArgs::sched_sk), compiled for rows of 256
-// bytes or more only; the other variant runs one piece per workgroup.
-template <typename T, int HD, int REP, int PR, bool SK>
-__global__ void __launch_bounds__(kThreads)
-decode_partials_kernel(DecodeArgs a) {
+// bytes or more only; the other variant runs one piece per workgroup. TAILS:
+// stream-K over shared-prefix tails (a.sh.group_start set), an instance of its
+// own so that the plain stream-K kernel carries none of its code (the TP=8
+// shard of the LLaMA-2-70B layer ran 29.8 us with one kernel for both, 28.7 us
+// apart).
+template <typename T, int HD, int REP, int PR, bool SK, bool TAILS>
+__device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   using G = Geo<T, HD, REP>;
   using L = Lds<T, HD, REP>;
   // PR > 0: paired KV heads (see DecodeArgs::pair_rep); chunk i of a lane's
@@ -1163,7 +1167,7 @@ decode_partials_kernel(DecodeArgs a) {
   int nsplit;
   if (sched) {
     nsplit = pc.n;
-    if (SK && a.sh.group_start) {
+    if constexpr (TAILS) {
       // a shared-prefix tail: the shared pass's partials lead
       start = pc.start;
       nps = (start + a.sh.prefix_part - 1) / a.sh.prefix_part;
@@ -1456,9 +1460,9 @@ decode_partials_kernel(DecodeArgs a) {
   int* st_lds = reinterpret_cast<int*>(smem + round16(Lds<T, HD, REP>::bytes(0)));
   int* len_lds = st_lds + a.num_seqs;
   int* first_lds = len_lds + a.num_seqs + kWaves;   // shared-prefix tails only
-  const bool tails = a.sh.group_start != nullptr;
-  const int U = sk_layout(a, lim, st_lds, len_lds, len_lds + a.num_seqs, first_lds,
-                          first_lds + a.num_seqs);
+  constexpr bool tails = TAILS;
+  const int U = sk_layout<TAILS>(a, lim, st_lds, len_lds, len_lds + a.num_seqs, first_lds,
+                                 first_lds + a.num_seqs);
   const int la = __builtin_ctz((unsigned)a.sched_align);
   const int i = blockIdx.y;
   const int Nh = a.sched_sk, H = Nh / 2, mu = a.sk_min_units;
@@ -1518,6 +1522,16 @@ decode_partials_kernel(DecodeArgs a) {
     piece();
   }
   }
+}
+
+template <typename T, int HD, int REP, int PR, bool SK>
+__global__ void __launch_bounds__(kThreads) decode_partials_kernel(DecodeArgs a) {
+  decode_body<T, HD, REP, PR, SK, false>(a);
+}
+
+template <typename T, int HD, int REP>
+__global__ void __launch_bounds__(kThreads) decode_tails_kernel(DecodeArgs a) {
+  decode_body<T, HD, REP, 0, true, true>(a);
 }
 
 // Merge split partials of sequences with more than one split: one wave per
@@ -1600,6 +1614,10 @@ pkv_status launch_split(const DecodeArgs& a, hipStream_t st) {
   }
   if (a.sched_sk > 0) {
     if constexpr (PR == 0 && HD * sizeof(T) >= 256) {
+      if (a.sh.group_start) {
+        hipLaunchKernelGGL((decode_tails_kernel<T, HD, REP>), grid, dim3(kThreads), lds, st, a);
+        return launch_status("decode_tails_kernel");
+      }
       hipLaunchKernelGGL((decode_partials_kernel<T, HD, REP, PR, true>), grid, dim3(kThreads),
                          lds, st, a);
       return launch_status("decode_partials_kernel");

@@ -221,16 +221,16 @@ def test_70b_layer_64_users_of_one_prompt():
     note(f"{wl.name}: all 64 sequences, max error {err:.3e}")
 
 
-@pytest.mark.parametrize("hkv,hq", [(1, 8), (8, 64)])
-def test_stream_k_tails(hkv, hq):
+@pytest.mark.parametrize("dtype,hd,hkv,hq", [(BF16, 128, 1, 8), (BF16, 128, 8, 64), (F32, 64, 2, 8)])
+def test_stream_k_tails(dtype, hd, hkv, hq):
     """Tails long enough for stream-K ranges (at least 256 KiB of K/V per range
     at the longest tail): three groups with prompts of 1024, 2048 and 512
     tokens; members of length 0, members whose context is exactly the prompt
     (empty tail: only the shared pass's partials) or inside it, and tails up
     to 6000 tokens laid end to end. Every sequence against the oracle."""
-    wl = make_shared([20, 30, 14], [1024, 2048, 512], ("uniform", 1, 6000), dtype=BF16,
-                     num_q_heads=hq, num_kv_heads=hkv, head_dim=128, seed=41 + hkv,
-                     name=f"stream-k tails hkv{hkv}")
+    wl = make_shared([20, 30, 14], [1024, 2048, 512], ("uniform", 1, 6000), dtype=dtype,
+                     num_q_heads=hq, num_kv_heads=hkv, head_dim=hd, seed=41 + hkv,
+                     name=f"stream-k tails {dtype} hd{hd} hkv{hkv}")
     wl.context_lens[1] = 0
     wl.context_lens[2] = 1024
     wl.context_lens[25] = 2048
