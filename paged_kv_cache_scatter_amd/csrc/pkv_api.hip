@@ -319,7 +319,7 @@ int64_t shared_min_saved_bytes() {
 }
 
 // Shared-prefix plan: the tail splits (partition from the longest tail), then
-// the shared pass's key splits, sized for about two workgroups per CU.
+// the shared pass's key splits, sized for about one workgroup per CU.
 // sd->group_start stays NULL when the shared pass is not used (no groups, a
 // prefix shorter than a block, or a shape the matrix-core pass does not
 // compile); the plan is then plain decode.
@@ -363,7 +363,12 @@ pkv_status plan_shared(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks
   const int64_t base = (int64_t)in.num_groups * pool->num_kv_heads * row_tiles;
   const int64_t max_ks = (in.max_prefix + align - 1) / align;
   const int64_t cus = num_cus();
-  const int64_t nks = std::min(std::max<int64_t>((2 * cus + base - 1) / base, 1), max_ks);
+  // key splits for about one shared-pass workgroup per CU: fewer splits leave
+  // each tail fewer partials to merge. LLaMA-2-70B layer, 64 users of a
+  // 4096-token prompt (3 rounds on one box, whole call): 4 splits (half a
+  // workgroup per CU) 143.2-143.6 us, 6: 139.2-139.7, 8: 137.9-138.5, 16:
+  // 144.4-145.1, 32: 159.4-160.2.
+  const int64_t nks = std::min(std::max<int64_t>((cus + base - 1) / base, 1), max_ks);
   int64_t pp = ((in.max_prefix + nks - 1) / nks + align - 1) / align * align;
   pp = std::min(pp, (int64_t)kSharedMaxTbl * bs / align * align);
   const int64_t jp = (in.max_prefix + pp - 1) / pp;

@@ -144,9 +144,9 @@ def test_shared_prefix_plan(lib, monkeypatch):
     monkeypatch.delenv("PKV_SHARED_MIN_SAVED_BYTES", raising=False)
     d = _desc(nb=32769, bs=16, hkv=8, hd=128)
     # tails: 2 splits of 1024 tokens; shared pass: 1 group x 8 KV heads x 4 row
-    # tiles (64 members x 8 heads / 128 rows) = 32 units, so 16 key splits of
-    # 128 tokens for about two workgroups per CU
-    rows = 64 * 64 * (16 + 2)
+    # tiles (64 members x 8 heads / 128 rows) = 32 units, so 8 key splits of
+    # 256 tokens for about one workgroup per CU
+    rows = 64 * 64 * (8 + 2)
     assert _shared_ws(lib, d) == COUNTER_AREA + rows * 2 * 4 + rows * 128 * 4
     # no groups, a prompt shorter than a block, an uncompiled head size: plain decode
     plain = lib.pkv_decode_workspace_bytes(64, 64, 4096, 1024, ctypes.byref(d))
@@ -156,7 +156,7 @@ def test_shared_prefix_plan(lib, monkeypatch):
     assert _shared_ws(lib, d32) == lib.pkv_decode_workspace_bytes(64, 64, 4096, 1024,
                                                                   ctypes.byref(d32))
     # the tail partition follows max_tail_len; < 0 means max_context_len
-    assert _shared_ws(lib, d, mt=-1) == COUNTER_AREA + 64 * 64 * (16 + 4) * (2 + 128) * 4
+    assert _shared_ws(lib, d, mt=-1) == COUNTER_AREA + 64 * 64 * (8 + 4) * (2 + 128) * 4
     # inconsistent sizes give 0 bytes
     for kw in (dict(mp=5000), dict(G=65), dict(mg=0), dict(mg=65), dict(mt=5000), dict(G=-1)):
         assert _shared_ws(lib, d, **kw) == 0, kw
