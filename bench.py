@@ -870,7 +870,7 @@ PHASES = ["entry", "piece and context length known", "queries and block ids arri
 
 
 def phase_trace(cfg: int):
-    """One launch of the decode (config 5: the fused step) through the traced
+    """One launch of the decode (the fused step for the LLaMA-2-70B layer) through the traced
     build (libpkv_trace.so: the same kernels recording the 100 MHz realtime
     counter at each phase boundary of every workgroup; a workgroup that runs
     several pieces keeps the phases of its first and the end of its last, and

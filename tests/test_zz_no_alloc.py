@@ -51,8 +51,9 @@ def _step_pair(wl):
 
 @pytest.mark.parametrize("cfg,sizes", [(5, (64, 9)), (4, (192, 40))])
 def test_noalloc_step_matches_workspace_step(cfg, sizes):
-    """Config 5 splits both calls (64 then 9 sequences); config 4 runs 192
-    sequences unsplit (no scratch needed), then 40 sequences split."""
+    """The LLaMA-2-70B layer splits both calls (64 then 9 sequences); the
+    Llama-3.2-1B shape runs 192 sequences unsplit (no scratch needed), then 40
+    sequences split."""
     for S in sizes:
         wl = make_workload(cfg, num_seqs=S)
         ((o_ws, k_ws, v_ws), (o_na, k_na, v_na)), ref = _step_pair(wl)
